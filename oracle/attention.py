@@ -1,0 +1,150 @@
+"""Exact attention forward in fp64 on the CPU -- test infrastructure only.
+
+What it computes (the definition, not an algorithm for computing it fast):
+
+  O = softmax(scale * Q K^T + mask) V,   LSE_i = log sum_j exp(scale * q_i . k_j + mask_ij)
+
+* The formula is the one stated at the top of "FlashAttention-3 Deep Dive"
+  (mojostudio.in, introduction): softmax(Q K^T / sqrt(d_k)) V; ``scale``
+  generalises 1/sqrt(d_k).  The pages call the method exact, so the oracle is
+  the plain definition with the full score matrix materialised.
+* The per-row log-sum-exp follows the softmax-statistics treatment listed in
+  the Hopper tag page (l1-ca0.github.io, contents entry 4.6 "rescaling,
+  correction, and LSE"); the section body is absent from the pages, so the
+  reading is: natural log, including ``scale``, one fp32 value per query row.
+* Causal: key j is masked for query i when j > i (top-left alignment; the
+  configurations all have Sq == Sk where every convention agrees).
+* GQA: query head h uses key/value head h // (Hq // Hkv) (consecutive groups;
+  contents entry 9.5 of the Hopper tag page names GQA without a body).
+* Varlen: cumulative offsets ``cu_seqlens`` cut the packed token axis into
+  independent sequences ("FlashAttention-3 Deep Dive", FAQ on ragged
+  batches); indices inside a sequence are local.
+* A row that sees no key (empty sequence, Sk == 0) gets O = 0, LSE = -inf.
+
+Rows are independent, so rows may be processed in chunks to bound memory, but
+each row is computed completely (no streaming rescale).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    """Upcast the exact values the kernel consumes (torch or numpy) to fp64."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", dtype=torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+               rows: Optional[np.ndarray] = None):
+    """Softmax probabilities for one head.
+
+    q [Sq, d], k [Sk, d] (fp64).  Returns (P [R, Sk], m [R], l [R]) for the
+    selected query rows (all rows if ``rows`` is None), where
+    P = exp(S - m) / l, S = scale * q k^T with -inf on masked entries,
+    m = row max of S, l = sum_j exp(S_ij - m_i).
+    """
+    Sq, Sk = q.shape[0], k.shape[0]
+    if rows is None:
+        rows = np.arange(Sq)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (q[rows] @ k.T)                      # [R, Sk]
+    if causal:
+        j = np.arange(Sk)[None, :]
+        s = np.where(j > rows[:, None], -np.inf, s)
+    m = s.max(axis=1) if Sk > 0 else np.full(len(rows), -np.inf)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m_safe[:, None])                  # exp(-inf) = 0 on masked entries
+    l = p.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(l[:, None] > 0, p / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return p, m, l
+
+
+def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+                   rows: Optional[np.ndarray] = None, row_chunk: int = 1024):
+    """Attention for one head: q [Sq, d], k/v [Sk, d] -> (O [R, d], LSE [R])."""
+    Sq = q.shape[0]
+    if rows is None:
+        rows = np.arange(Sq)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    L = np.full(len(rows), -np.inf, dtype=np.float64)
+    for c0 in range(0, len(rows), row_chunk):
+        r = rows[c0:c0 + row_chunk]
+        p, m, l = head_probs(q, k, scale, causal, r)
+        O[c0:c0 + len(r)] = p @ v
+        with np.errstate(divide="ignore"):
+            L[c0:c0 + len(r)] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return O, L
+
+
+def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None,
+              heads: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
+              batches: Optional[Sequence[int]] = None):
+    """Exact attention forward in fp64.
+
+    Dense:  q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d]  ->  O [B, Sq, Hq, d], LSE [B, Hq, Sq]
+    Varlen: q [T, Hq, d],     k/v [T, Hkv, d], cu_seqlens [nseq+1]
+                                                    ->  O [T, Hq, d],    LSE [Hq, T]
+
+    ``heads`` / ``batches`` / ``rows`` restrict the work to a subset (dense
+    only); entries outside the subset are left as NaN so that a caller can
+    compare only what was computed.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        T, Hq, d = q.shape
+        O = np.zeros((T, Hq, d))
+        L = np.full((Hq, T), -np.inf)
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            if b <= a:
+                continue
+            o_s, l_s = attention(q[None, a:b], k[None, a:b], v[None, a:b], scale, causal)
+            O[a:b] = o_s[0]
+            L[:, a:b] = l_s[0]
+        return O, L
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    hs = range(Hq) if heads is None else heads
+    bs = range(B) if batches is None else batches
+    partial = heads is not None or rows is not None or batches is not None
+    O = np.full((B, Sq, Hq, v.shape[3]), np.nan if partial else 0.0)
+    L = np.full((B, Hq, Sq), np.nan if partial else -np.inf)
+    rsel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    for b in bs:
+        for h in hs:
+            hk = h // group
+            o, l = head_attention(q[b, :, h], k[b, :, hk], v[b, :, hk], scale, causal, rsel)
+            O[b, rsel, h] = o
+            L[b, h, rsel] = l
+    return O, L
+
+
+def attention_flops(Sq: int, Sk: int, d: int, causal: bool, B: int = 1, H: int = 1,
+                    lengths: Optional[Sequence[int]] = None) -> float:
+    """Algorithmic FLOPs: 4*d per unmasked (query, key) pair (two GEMMs,
+    multiply + add each); masked pairs are not counted."""
+    def pairs(sq, sk):
+        if not causal:
+            return sq * sk
+        n = min(sq, sk)
+        return n * (n + 1) // 2 + max(0, sq - sk) * sk
+    if lengths is not None:
+        return 4.0 * d * H * sum(pairs(n, n) for n in lengths)
+    return 4.0 * d * B * H * pairs(Sq, Sk)
