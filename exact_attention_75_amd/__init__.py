@@ -1,0 +1,188 @@
+"""MI355X-native fused exact-attention forward.
+
+Thin ctypes binding over the C ABI of ``libattn.so`` (declared in
+``include/attn.h``).  It only marshals arguments: output tensors are
+allocated with torch (device memory), pointers, sizes and the current HIP
+stream are handed to the library, and every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+
+    o, lse = fwd(q, k, v, causal=True)            # bf16 / fp16, dense or varlen
+    o, lse = fwd(q32, k32, v32, dtype="fp8")      # fp32 inputs, fp8 GEMMs, bf16 out
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["fwd", "fwd_fp8", "fp8_prepass", "library", "default_signs", "tile_of",
+           "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
+
+ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3, ATTN_FP8_E4M3_HADAMARD = 0, 1, 2, 3
+_DTYPE_NAMES = {"bf16": ATTN_BF16, "fp16": ATTN_FP16, "fp8": ATTN_FP8_E4M3,
+                "fp8_hadamard": ATTN_FP8_E4M3_HADAMARD}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed with status {code}: {library().attn_strerror(code).decode()}")
+        self.code = code
+
+
+def library() -> ctypes.CDLL:
+    """Load libattn.so (built by ``python -m exact_attention_75_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with python -m exact_attention_75_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    L.attn_fwd.restype = I
+    L.attn_fp8_prepass.argtypes = [P, P, P, I, I, I, I, I, P, P]
+    L.attn_fp8_prepass.restype = I
+    L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    L.attn_fwd_fp8.restype = I
+    L.attn_default_signs.argtypes = [ctypes.POINTER(ctypes.c_float), I]
+    L.attn_default_signs.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    L.attn_tile_of.argtypes = [I, I, I, I, I, I, I, IP, IP, IP]
+    L.attn_tile_of.restype = I
+    L.attn_grid_size.argtypes = [I, I, I, I, I, IP, IP]
+    L.attn_grid_size.restype = I
+    L.attn_strerror.argtypes = [I]
+    L.attn_strerror.restype = ctypes.c_char_p
+    L.attn_release.argtypes = []
+    L.attn_release.restype = None
+    _lib = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise AttnError(code, what)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+        dtype: Optional[str] = None, return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention forward through ``attn_fwd``.
+
+    Dense: q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> o [B, Sq, Hq, d], lse [B, Hq, Sq].
+    Varlen (cu_seqlens int32 [nseq+1] on the device): q [T, Hq, d], k/v [T, Hkv, d]
+    -> o [T, Hq, d], lse [Hq, T].
+    dtype: None infers bf16/fp16 from q; "fp8" / "fp8_hadamard" take fp32 inputs
+    and return bf16 o.
+    """
+    _need_gpu(q, k, v, cu_seqlens)
+    if dtype is None:
+        if q.dtype == torch.bfloat16:
+            dt = ATTN_BF16
+        elif q.dtype == torch.float16:
+            dt = ATTN_FP16
+        else:
+            raise ValueError("q must be bf16 or fp16 (or pass dtype='fp8' with fp32 inputs)")
+    else:
+        dt = _DTYPE_NAMES[dtype]
+    if dt in (ATTN_BF16, ATTN_FP16):
+        want = torch.bfloat16 if dt == ATTN_BF16 else torch.float16
+        if q.dtype != want or k.dtype != want or v.dtype != want:
+            raise ValueError("q, k, v must share the kernel dtype")
+        out_dtype = want
+    else:
+        if q.dtype != torch.float32 or k.dtype != torch.float32 or v.dtype != torch.float32:
+            raise ValueError("the fp8 path takes fp32 q, k, v")
+        out_dtype = torch.bfloat16
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        B, Sq, Sk = cu_seqlens.numel() - 1, T, k.shape[0]
+        lse_shape = (Hq, T)
+    else:
+        B, Sq, Hq, d = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+        lse_shape = (B, Hq, Sq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device) if return_lse else None
+    rc = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                            float(scale), int(bool(causal)), _ptr(cu_seqlens), dt, _stream())
+    _check(rc, "attn_fwd")
+    return o, lse
+
+
+def fp8_prepass(x: torch.Tensor, transpose_out: bool = False,
+                signs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-quantise x [B, S, H, d] fp32 -> (codes uint8, descale fp32 [B, H, ceil(S/128)]).
+
+    codes are [B, S, H, d], or [B, H, d, S] when transpose_out."""
+    _need_gpu(x, signs)
+    if x.dtype != torch.float32:
+        raise ValueError("x must be fp32")
+    B, S, H, d = x.shape
+    shape = (B, H, d, S) if transpose_out else (B, S, H, d)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    ds = torch.empty((B, H, (S + 127) // 128), dtype=torch.float32, device=x.device)
+    rc = library().attn_fp8_prepass(_ptr(x), _ptr(x8), _ptr(ds), B, S, H, d, int(bool(transpose_out)),
+                                    _ptr(signs), _stream())
+    _check(rc, "attn_fp8_prepass")
+    return x8, ds
+
+
+def fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, causal: bool = False,
+            scale: Optional[float] = None, return_lse: bool = True):
+    """Attention forward on pre-quantised operands through ``attn_fwd_fp8``.
+
+    q8 [B, Sq, Hq, d], k8 [B, Sk, Hkv, d], v8t [B, Hkv, d, Sk] (uint8 E4M3 codes),
+    descales fp32 [B, H, ceil(S/128)] -> o bf16 [B, Sq, Hq, d], lse [B, Hq, Sq]."""
+    _need_gpu(q8, k8, v8t, q_descale, k_descale, v_descale)
+    B, Sq, Hq, d = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device) if return_lse else None
+    rc = library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_descale), _ptr(k_descale),
+                                _ptr(v_descale), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                                float(scale), int(bool(causal)), _stream())
+    _check(rc, "attn_fwd_fp8")
+    return o, lse
+
+
+def default_signs(n: int = 128):
+    buf = (ctypes.c_float * n)()
+    _check(library().attn_default_signs(buf, n), "attn_default_signs")
+    return [float(x) for x in buf]
+
+
+def tile_of(p: int, B: int, Hq: int, Hkv: int, Sq: int, block_m: int, causal: bool):
+    b, h, m = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = library().attn_tile_of(p, B, Hq, Hkv, Sq, block_m, int(causal), ctypes.byref(b),
+                                ctypes.byref(h), ctypes.byref(m))
+    _check(rc, "attn_tile_of")
+    return b.value, h.value, m.value

@@ -1,0 +1,291 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument validation,
+// tile planning, dispatch over the kernel variants, the fp8 workspace and
+// error reporting.  Validation and planning touch no HIP state, so every
+// error path returns before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return ATTN_ERR_HIP;
+}
+
+constexpr long long kMax32 = 0x7fffffffLL;
+
+int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_ARG;
+  // per-tensor element counts and in-kernel 32-bit row offsets
+  if ((long long)Sq * Hq * d > kMax32 || (long long)Sk * Hkv * d > kMax32) return ATTN_ERR_SIZE;
+  if ((long long)B * Hq * ((Sq + attn::kBlockM - 1) / attn::kBlockM) > kMax32) return ATTN_ERR_SIZE;
+  return ATTN_OK;
+}
+
+// --- fp8 workspace: one lazily grown device buffer per device -------------
+constexpr int kMaxDevices = 64;
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+Workspace g_ws[kMaxDevices];
+std::mutex g_ws_mu;
+
+int workspace(size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      // the old buffer may still be in use by enqueued work
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e);
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    e = hipMalloc(&w.ptr, bytes);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      return ATTN_ERR_NOMEM;
+    }
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return ATTN_OK;
+}
+
+uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x * 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// device copy of the default sign vector, per device
+float* g_signs[kMaxDevices] = {};
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (non-positive size, or varlen with Sq != Sk)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension (64 or 128; fp8 needs 128)";
+    case ATTN_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case ATTN_ERR_DTYPE: return "unknown or unsupported dtype for this call";
+    case ATTN_ERR_ARG: return "invalid argument (scale must be finite and > 0, or unsupported combination)";
+    case ATTN_ERR_NOMEM: return "device workspace allocation failed";
+    case ATTN_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
+    case ATTN_ERR_SIZE: return "problem too large for 32-bit in-kernel indexing";
+    default: return "unknown status code";
+  }
+}
+
+int attn_default_signs(float* signs_host, int n) {
+  if (!signs_host) return ATTN_ERR_NULL;
+  if (n <= 0 || n > 128) return ATTN_ERR_SHAPE;
+  for (int i = 0; i < n; ++i)
+    signs_host[i] = (splitmix64((55ULL << 32) + (uint64_t)i + 1) >> 63) ? -1.f : 1.f;
+  return ATTN_OK;
+}
+
+int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* block_m_out) {
+  if (!grid_out || !block_m_out) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Sq <= 0) return ATTN_ERR_SHAPE;
+  (void)d;
+  (void)dtype;
+  *block_m_out = attn::kBlockM;
+  *grid_out = B * Hq * ((Sq + attn::kBlockM - 1) / attn::kBlockM);
+  return ATTN_OK;
+}
+
+int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal, int* b_out,
+                 int* h_out, int* m_out) {
+  if (!b_out || !h_out || !m_out) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || block_m <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  attn::TileMap tm = attn::make_tile_map(B, Hq, Hkv, Sq, block_m, causal);
+  if (p < 0 || p >= tm.ntiles) return ATTN_ERR_SHAPE;
+  attn::tile_decode(tm, p, *b_out, *h_out, *m_out);
+  return ATTN_OK;
+}
+
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const float* q_descale,
+                 const float* k_descale, const float* v_descale, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int d, float scale, int causal, void* stream) {
+  if (!q8 || !k8 || !v8t || !q_descale || !k_descale || !v_descale || !o) return ATTN_ERR_NULL;
+  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  attn::Fp8FwdParams p{};
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8t = v8t;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.group = Hq / Hkv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBlockM, causal);
+  p.grid = p.tm.ntiles;
+  hipError_t e = attn::launch_fwd_fp8(p, causal, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, int H, int d,
+                     int transpose_out, const float* signs, void* stream) {
+  if (!x || !x8 || !descale) return ATTN_ERR_NULL;
+  if (B <= 0 || S <= 0 || H <= 0) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if ((long long)B * S * H * d > kMax32 * 2) return ATTN_ERR_SIZE;
+  attn::PrepassParams p{};
+  p.x = x;
+  p.x8 = x8;
+  p.descale = descale;
+  p.signs = signs;
+  p.B = B;
+  p.S = S;
+  p.H = H;
+  p.d = d;
+  p.transpose_out = transpose_out ? 1 : 0;
+  hipError_t e = attn::launch_prepass(p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int Sq, int Sk, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+             void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (dtype < ATTN_BF16 || dtype > ATTN_FP8_E4M3_HADAMARD) return ATTN_ERR_DTYPE;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (B <= 0) return ATTN_ERR_SHAPE;
+    if (Sq != Sk) return ATTN_ERR_SHAPE;
+  }
+  int rc = check_common(varlen ? 1 : B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E4M3_HADAMARD) {
+    if (varlen) return ATTN_ERR_ARG;
+    if (d != 128) return ATTN_ERR_HEADDIM;
+    const long long nbq = (Sq + 127) / 128, nbk = (Sk + 127) / 128;
+    const size_t qb = (size_t)B * Sq * Hq * d, kb = (size_t)B * Sk * Hkv * d;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t sq_b = al(sizeof(float) * B * Hq * nbq), sk_b = al(sizeof(float) * B * Hkv * nbk);
+    const size_t total = al(qb) + 2 * al(kb) + sq_b + 2 * sk_b;
+    void* ws = nullptr;
+    rc = workspace(total, &ws);
+    if (rc) return rc;
+    uint8_t* base = (uint8_t*)ws;
+    uint8_t* q8 = base;
+    uint8_t* k8 = q8 + al(qb);
+    uint8_t* v8t = k8 + al(kb);
+    float* qs = (float*)(v8t + al(kb));
+    float* ks = (float*)((uint8_t*)qs + sq_b);
+    float* vs = (float*)((uint8_t*)ks + sk_b);
+    const float* sg = nullptr;
+    if (dtype == ATTN_FP8_E4M3_HADAMARD) {
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_fail(e);
+      if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_ARG;
+      std::lock_guard<std::mutex> lk(g_ws_mu);
+      if (!g_signs[dev]) {
+        float hs[128];
+        attn_default_signs(hs, 128);
+        float* dp = nullptr;
+        e = hipMalloc(&dp, sizeof hs);
+        if (e != hipSuccess) return ATTN_ERR_NOMEM;
+        e = hipMemcpy(dp, hs, sizeof hs, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+          (void)hipFree(dp);
+          return hip_fail(e);
+        }
+        g_signs[dev] = dp;
+      }
+      sg = g_signs[dev];
+    }
+    rc = attn_fp8_prepass((const float*)q, q8, qs, B, Sq, Hq, d, 0, sg, stream);
+    if (!rc) rc = attn_fp8_prepass((const float*)k, k8, ks, B, Sk, Hkv, d, 0, sg, stream);
+    if (!rc) rc = attn_fp8_prepass((const float*)v, v8t, vs, B, Sk, Hkv, d, 1, nullptr, stream);
+    if (!rc) rc = attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream);
+    return rc;
+  }
+
+  attn::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.group = Hq / Hkv;
+  p.q_tok_stride = Hq * d;
+  p.kv_tok_stride = Hkv * d;
+  p.q_batch_stride = (long long)Sq * Hq * d;
+  p.kv_batch_stride = (long long)Sk * Hkv * d;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (varlen) {
+    // one tile per (head, query block of a sequence); the number of blocks is
+    // at most ceil(T / BM) + (number of sequences), the rest exit at once
+    const long long nb = (Sq + attn::kBlockM - 1) / attn::kBlockM + B;
+    if (nb * Hq > kMax32) return ATTN_ERR_SIZE;
+    p.grid = (int)(nb * Hq);
+  } else {
+    p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBlockM, causal);
+    p.grid = p.tm.ntiles;
+  }
+  hipError_t e = attn::launch_fwd(p, dtype, d, causal, varlen ? 1 : 0, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+void attn_release(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    if (!g_ws[dev].ptr && !g_signs[dev]) continue;
+    if (hipSetDevice(dev) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();
+    if (g_ws[dev].ptr) (void)hipFree(g_ws[dev].ptr);
+    if (g_signs[dev]) (void)hipFree(g_signs[dev]);
+    g_ws[dev] = Workspace{};
+    g_signs[dev] = nullptr;
+  }
+  (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,360 @@
+// attn_fwd.hip -- fused exact-attention forward for gfx950 (MI355X), bf16/fp16.
+//
+// What is computed: O = softmax(scale * Q K^T + mask) V and the per-row
+// natural-log LSE ("FlashAttention-3 Deep Dive", introduction formula; Hopper
+// tag page contents 4.2 and 4.6 for the streaming state and the LSE), tile by
+// tile so that the score matrix stays on chip.
+//
+// Mapping onto CDNA4 (the pages' Hopper schedule is prior art, not a plan):
+//
+//  * A workgroup is 4 waves (256 threads) and owns BM = 128 query rows of one
+//    (batch, head); each wave owns 32 of them.  Two workgroups share a CU, so
+//    each SIMD runs two waves: while one wave is in its softmax (VALU) the
+//    other issues MFMA -- the role the pages give to ping-pong warpgroups
+//    ("flash-attention-3", "Why a schedule"), here obtained from the
+//    hardware's wave interleaving instead of named barriers.
+//  * Both GEMMs run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation.
+//    The first is computed transposed, S^T = K Q^T: the accumulator then
+//    holds one query per lane (column) and 16 of the tile's keys per lane, so
+//    the row max and row sum are in-lane, plus one exchange between the two
+//    lane halves (v_permlane32_swap).  The second is O^T = V^T P^T: the
+//    probabilities P^T are already in the lane layout of the MFMA B operand
+//    and never leave registers (the pages' "P stays in registers" rule), and
+//    the O accumulator also holds one query per lane, so the per-row
+//    rescale and the final 1/l are lane scalars.
+//  * Keys are fed to the first MFMA in a permuted row order (bits 2 and 3 of
+//    the row index swapped) so that each lane half's 16 probabilities of a
+//    16-key chunk are 8 consecutive keys -- exactly the K-operand order of the
+//    second MFMA, with no shuffle.
+//  * K/V tiles of BN keys are copied global -> LDS by the direct-to-LDS loads
+//    (global_load_lds_dwordx4), double-buffered: tile t+1 streams in while
+//    tile t is computed (the pages' producer role, done by the memory
+//    pipeline rather than a producer warpgroup).  16-byte chunks are XOR
+//    swizzled per row; the swizzle is expressed through the global address
+//    each lane fetches, since the LDS side of the copy is lane-linear.
+//  * The V operand of the second GEMM needs 8 consecutive keys per lane for a
+//    fixed head-dim column; ds_read_b64_tr_b16 (gfx950's transposing LDS
+//    read) delivers that from the row-major V tile.
+//  * Online softmax in the exp2 domain with scale*log2(e) folded into one
+//    FMA, and a lazy rescale: the running max is only moved (and O, l
+//    rescaled) when a row's new max exceeds it by more than 2^8 in
+//    probability, which is exact arithmetic (any reference point cancels in
+//    O = sum P V / sum P) and keeps P <= 256.
+//  * Causal: a wave skips key tiles entirely above its diagonal; only tiles
+//    that cross the diagonal or the sequence end are masked (the pages' split
+//    loop, Hopper tag page contents 4.7).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Swizzle of 16-byte chunks inside one LDS row of the K tile: chunk c of row
+// r is stored at position c ^ swz_k(r).  16 consecutive rows (the lanes that
+// read one chunk column together) land on 16 different chunk positions.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return (D == 128) ? (r & 15) : (r & 7);
+}
+
+// Swizzle of the V tile.  A transposing read covers 4 consecutive rows x 64
+// bytes (chunks 4j..4j+3); the XOR moves each of those rows to a different
+// 64-byte quarter of the bank space.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return (D == 128) ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// Row order of keys in the first MFMA: MFMA row r reads key pi(r) of its
+// 32-key block, pi swapping bits 2 and 3.
+__device__ __forceinline__ int key_perm(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ float wave_half_swap(float x) {
+  // value of lane l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  const int lane = threadIdx.x & 63;
+  return __int_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+template <typename T, int D, int BN, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_kernel(FwdParams p) {
+  typedef typename Mma<T>::vec8 vec8;
+  constexpr int NW = 4;
+  constexpr int BM = kBlockM;
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int KT = D / 16;           // k-steps of the first GEMM
+  constexpr int NB = BN / 32;          // 32-key blocks per tile
+  constexpr int NC = BN / 16;          // 16-key chunks per tile (second GEMM)
+  constexpr int DB = D / 32;           // 32-column blocks of O^T
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int TILE_BYTES = BN * ROW_BYTES;
+  constexpr int LOADS = BN * CPR / (NW * 64);   // DMA instructions per wave per tensor
+  constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
+  constexpr float NEG_INF = -__builtin_inff();
+  static_assert(BN % 32 == 0 && (BN * CPR) % (NW * 64) == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];  // [stage][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---------------------------------------------------------------- tile decode
+  int b, hq, mblk, q_len, kv_len;
+  long long q_off, kv_off;   // element offsets of token 0 of this (batch | sequence)
+  long long lse_off;         // index of this head's token 0 in lse
+  if (VARLEN) {
+    const int pid = blockIdx.x;
+    hq = pid % p.Hq;
+    int r = pid / p.Hq;
+    int s = 0, start = 0, len = 0, nb = 0;
+    for (; s < p.B; ++s) {
+      start = p.cu_seqlens[s];
+      len = p.cu_seqlens[s + 1] - start;
+      nb = (len + BM - 1) / BM;
+      if (r < nb) break;
+      r -= nb;
+    }
+    if (s >= p.B) return;     // beyond the last tile (uniform over the workgroup)
+    mblk = nb - 1 - r;         // longest query block of the sequence first
+    b = 0;
+    q_len = len;
+    kv_len = len;
+    q_off = (long long)start * p.q_tok_stride;
+    kv_off = (long long)start * p.kv_tok_stride;
+    lse_off = (long long)hq * p.Sq + start;
+  } else {
+    tile_decode(p.tm, blockIdx.x, b, hq, mblk);
+    q_len = p.Sq;
+    kv_len = p.Sk;
+    q_off = (long long)b * p.q_batch_stride;
+    kv_off = (long long)b * p.kv_batch_stride;
+    lse_off = ((long long)b * p.Hq + hq) * p.Sq;
+  }
+  const int hkv = hq / p.group;
+  const T* Qp = (const T*)p.q + q_off + hq * D;
+  const T* Kp = (const T*)p.k + kv_off + hkv * D;
+  const T* Vp = (const T*)p.v + kv_off + hkv * D;
+  T* Op = (T*)p.o + q_off + hq * D;
+  const int qs = p.q_tok_stride;
+  const int ks = p.kv_tok_stride;
+
+  const int q0 = mblk * BM;
+  const int qw = q0 + wave * 32;                       // first query row of this wave
+  const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;  // one past the block's last row
+  const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
+  const int ntile = (kv_end + BN - 1) / BN;
+
+  // ---------------------------------------------------------------- Q fragment
+  // B operand of S^T = K Q^T: lane holds query l32, head-dim 16*kk + 8*h .. +7.
+  vec8 qf[KT];
+  {
+    const int qrow = (qw + l32 < q_len) ? qw + l32 : q_len - 1;
+    const T* qr = Qp + (long long)qrow * qs + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) qf[kk] = *(const vec8*)(qr + 16 * kk);
+  }
+
+  // ---------------------------------------------------------------- K/V copy
+  auto issue_tile = [&](int t, int stage) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = wave * LOADS + i;           // 64-chunk block written by this instruction
+      const int pos = blk * 64 + lane;            // LDS chunk position (lane-linear)
+      const int row = pos / CPR;
+      const int phys = pos % CPR;
+      const int grow = (j0 + row < kv_len) ? j0 + row : kv_len - 1;
+      const T* ksrc = Kp + (long long)grow * ks + ((phys ^ swz_k<D>(row)) * 8);
+      const T* vsrc = Vp + (long long)grow * ks + ((phys ^ swz_v<D>(row)) * 8);
+      __builtin_amdgcn_global_load_lds((const void*)ksrc, (LDS_AS void*)(smem[stage][0] + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vsrc, (LDS_AS void*)(smem[stage][1] + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  float m_run = NEG_INF;   // running max of scale*log2(e)*s for query l32 (same in both halves)
+  float l_run = 0.f;       // this lane half's share of the running sum
+  const float c = p.scale_log2;
+  const int qi = qw + l32;
+
+  // per-lane LDS addressing, invariant over tiles
+  int k_off[KT][NB];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int r = 32 * bb + key_perm(l32);
+      k_off[kk][bb] = r * ROW_BYTES + (((2 * kk + h) ^ swz_k<D>(r)) << 4);
+    }
+  const int G = lane >> 4, i16 = lane & 15;
+  int v_off[NC][DB];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int r = 16 * cc + 8 * h + (i16 >> 2);
+      const int dd = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
+      v_off[cc][db] = r * ROW_BYTES + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
+    }
+
+  if (ntile > 0) issue_tile(0, 0);
+
+  for (int t = 0; t < ntile; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntile) issue_tile(t + 1, (t + 1) & 1);
+    const int j0 = t * BN;
+    if (CAUSAL && j0 > qw + 31) continue;   // tile entirely above this wave's diagonal
+
+    const char* Ks = smem[t & 1][0];
+    const char* Vs = smem[t & 1][1];
+
+    // ---- S^T = K Q^T
+    f32x16 s[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) s[bb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const vec8 a = *(const vec8*)(Ks + k_off[kk][bb]);
+        s[bb] = Mma<T>::run(a, qf[kk], s[bb]);
+      }
+
+    // ---- mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
+    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
+    if (edge) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * bb + 16 * (i >> 3) + 8 * h + (i & 7);
+          const bool dead = (key >= kv_len) || (CAUSAL && key > qi);
+          s[bb][i] = dead ? NEG_INF : s[bb][i];
+        }
+    }
+
+    // ---- row max (in-lane over 32 keys, then across the two lane halves)
+    float mx = NEG_INF;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
+    mx = fmaxf(mx, wave_half_swap(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float msub = (m_run == NEG_INF) ? 0.f : m_run;
+
+    // ---- P = exp2(c*s - m), row sum, convert to the operand type
+    vec8 pk[NC];
+    float rs = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + e], c, -msub));
+        rs += pe;
+        pk[cc][e] = (T)pe;
+      }
+    l_run += rs;
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Vs + v_off[cc][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Vs + v_off[cc][db] + 4 * ROW_BYTES));
+        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = Mma<T>::run(__builtin_bit_cast(vec8, w), pk[cc], o[db]);
+      }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const float l_tot = l_run + wave_half_swap(l_run);
+  if (qi < q_len) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    T* orow = Op + (long long)qi * qs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        T4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (T)(o[db][4 * g + e] * inv);
+        *(T4*)(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (p.lse != nullptr && h == 0) {
+      const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+      p.lse[lse_off + qi] = lse;
+    }
+  }
+}
+
+template <typename T, int D, int BN>
+static hipError_t launch_t(const FwdParams& p, int causal, int varlen, hipStream_t s) {
+  dim3 grid(p.grid), block(kThreads);
+  if (varlen) {
+    if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BN, false, true>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BN, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (dtype == 0) {
+    return d == 128 ? launch_t<__bf16, 128, 64>(p, causal, varlen, s)
+                    : launch_t<__bf16, 64, 64>(p, causal, varlen, s);
+  }
+  return d == 128 ? launch_t<_Float16, 128, 64>(p, causal, varlen, s)
+                  : launch_t<_Float16, 64, 64>(p, causal, varlen, s);
+}
+
+}  // namespace attn

@@ -1,0 +1,165 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused exact-attention forward.
+ *
+ * The operation is exact attention, O = softmax(scale * Q K^T + mask) V, as
+ * written at the top of "FlashAttention-3 Deep Dive" (mojostudio.in,
+ * introduction), computed tile by tile with a streaming softmax so that the
+ * Sq x Sk score matrix never reaches device memory ("flash-attention-3",
+ * ai.thesatyajit.com, opening section: tile the computation and keep a running
+ * softmax).  Alongside O the library writes the per-row log-sum-exp
+ * LSE_i = log sum_j exp(scale * q_i . k_j + mask_ij) (natural log, scale
+ * included), the softmax statistic listed in the Hopper tag page
+ * (l1-ca0.github.io, contents entry 4.6).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never frees or retains them.  They must stay valid until the
+ *     stream has executed the enqueued work.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous: it validates its arguments on the host,
+ *     enqueues kernels on `stream` and returns; results are ready after the
+ *     stream is synchronised.  No call blocks or copies host<->device.
+ *   - Return value 0 (ATTN_OK) on success, a negative ATTN_ERR_* code on
+ *     failure.  Validation happens before anything is enqueued, so a call
+ *     that returns an error has written nothing.  Nothing throws or aborts
+ *     across the ABI; attn_strerror() turns a code into text (for
+ *     ATTN_ERR_HIP it includes the HIP runtime's message of the last failure).
+ *   - Layouts are contiguous, innermost dimension last, tokens-major (the
+ *     (batch, seqlen, heads, headdim) layout of the benchmark on the
+ *     "Lecture 9 -- Hopper / FlashAttention-3 / FlashAttention-4" page,
+ *     "Benchmark task").
+ *   - Grouped-query attention: query head h reads key/value head
+ *     h / (Hq / Hkv) (consecutive groups; Hq must be a multiple of Hkv).
+ *   - Causal masking hides key j from query i when j > i (indices local to
+ *     the sequence; top-left aligned when Sq != Sk).
+ *   - A query row that sees no key gets O = 0 and LSE = -inf.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  ATTN_BF16 / ATTN_FP16: q, k, v and o all hold that type.
+ * ATTN_FP8_E4M3 / ATTN_FP8_E4M3_HADAMARD: q, k, v hold fp32 values; the
+ * library quantises them to OCP E4M3 with one fp32 scale per 128 rows of one
+ * (batch, head) -- the per-block scaling of "FlashAttention-3 Deep Dive",
+ * section 4 -- optionally after the signed 128-point Hadamard rotation of Q
+ * and K (same section, incoherence processing), runs both GEMMs in fp8 with
+ * fp32 accumulation, and writes o as bf16. */
+enum attn_dtype {
+  ATTN_BF16 = 0,
+  ATTN_FP16 = 1,
+  ATTN_FP8_E4M3 = 2,
+  ATTN_FP8_E4M3_HADAMARD = 3
+};
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,     /* a required pointer is NULL                        */
+  ATTN_ERR_SHAPE = -2,    /* non-positive B/Hq/Hkv/Sq/Sk, varlen with Sq != Sk */
+  ATTN_ERR_HEADDIM = -3,  /* d not supported (64 or 128; 128 for fp8)          */
+  ATTN_ERR_GQA = -4,      /* Hq not a multiple of Hkv                          */
+  ATTN_ERR_DTYPE = -5,    /* unknown dtype, or dtype not valid for the call    */
+  ATTN_ERR_ARG = -6,      /* scale not finite or not > 0; unsupported combo    */
+  ATTN_ERR_NOMEM = -7,    /* workspace allocation failed                       */
+  ATTN_ERR_HIP = -8,      /* a HIP runtime call or kernel launch failed        */
+  ATTN_ERR_SIZE = -9      /* a size or index would overflow 32-bit addressing  */
+};
+
+/*
+ * attn_fwd -- fused attention forward.
+ *
+ * Dense (cu_seqlens == NULL):
+ *   q [B, Sq, Hq, d], k and v [B, Sk, Hkv, d], o [B, Sq, Hq, d],
+ *   lse [B, Hq, Sq] (fp32).
+ * Varlen (cu_seqlens != NULL): B is the number of sequences and
+ *   Sq == Sk == T, the total number of packed tokens.  cu_seqlens is a DEVICE
+ *   array of B + 1 int32 offsets with cu[0] = 0, cu[B] = T, non-decreasing;
+ *   sequence s owns tokens [cu[s], cu[s+1]) of q, k and v, and attends only
+ *   within itself ("FlashAttention-3 Deep Dive", FAQ on ragged batches).
+ *   q [T, Hq, d], k and v [T, Hkv, d], o [T, Hq, d], lse [Hq, T].
+ *   The offsets are read on the device and are not validated (reading them on
+ *   the host would need a synchronisation).  Varlen needs dtype bf16/fp16.
+ * scale: multiplies Q K^T before the softmax; must be finite and > 0
+ *   (1/sqrt(d) gives the formula's 1/sqrt(d_k)).
+ * causal: non-zero hides key j from query i when j > i.
+ * dtype: an attn_dtype.  For the fp8 types q, k, v are fp32 and o is bf16;
+ *   the quantised copies live in a library-owned, lazily grown device
+ *   workspace (released by attn_release); the Hadamard variant uses the
+ *   library's default sign vector (attn_default_signs).  fp8 needs d == 128.
+ * lse may be NULL when the caller does not want it.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             const int32_t* cu_seqlens, int dtype, void* stream);
+
+/*
+ * attn_fp8_prepass -- per-block fp8 quantisation ("FlashAttention-3 Deep
+ * Dive", section 4: per-block scaling and the Hadamard rotation).
+ *
+ * x [B, S, H, d] fp32 (device).  For every (b, h) and every block of 128
+ * consecutive rows (the last block may be shorter):
+ *   optional rotation  x <- (x * signs) H_d / sqrt(d)   (signs: d device
+ *                      floats of +-1; NULL = no rotation), in fp32;
+ *   s = amax / 448 over the block's rows and all d channels (s = 1 when the
+ *   block is all zero); code = E4M3(clip(x / s, -448, 448)), round to
+ *   nearest even.
+ * Outputs (device, caller-owned):
+ *   x8: uint8 codes, [B, S, H, d] when transpose_out == 0, or
+ *       [B, H, d, S] (token index innermost) when transpose_out != 0;
+ *   descale: fp32 [B, H, ceil(S / 128)], the scales s (dequantised value =
+ *       decode(code) * s).
+ * d must be 128 (the rotation is the 128-point transform).
+ */
+int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, int H, int d,
+                     int transpose_out, const float* signs, void* stream);
+
+/*
+ * attn_fwd_fp8 -- fused attention forward on pre-quantised E4M3 operands,
+ * fp32 accumulation in both GEMMs, bf16 output.
+ *   q8 [B, Sq, Hq, d] codes, k8 [B, Sk, Hkv, d] codes,
+ *   v8t [B, Hkv, d, Sk] codes (token index innermost: the K-major operand
+ *       the second GEMM wants, written by attn_fp8_prepass with
+ *       transpose_out = 1),
+ *   q_descale [B, Hq, ceil(Sq/128)], k_descale and v_descale
+ *       [B, Hkv, ceil(Sk/128)] fp32 block scales,
+ *   o [B, Sq, Hq, d] bf16, lse [B, Hq, Sq] fp32 (may be NULL).
+ * d must be 128; dense only (no cu_seqlens).
+ */
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                 float scale, int causal, void* stream);
+
+/* The library's default Hadamard sign vector used by ATTN_FP8_E4M3_HADAMARD:
+ * writes n (<= 128) host floats of +-1, sign i being the top bit of the
+ * splitmix64 output for counter (55 << 32) + i + 1.  Returns ATTN_OK, or
+ * ATTN_ERR_NULL / ATTN_ERR_SHAPE. */
+int attn_default_signs(float* signs_host, int n);
+
+/* Tile order of the forward kernel's scheduler, evaluated on the host (for
+ * inspection and tests): for workgroup index p of a dense launch, writes the
+ * (batch, query head, query block) it processes.  block_m is the number of
+ * query rows per tile.  Returns ATTN_OK or ATTN_ERR_SHAPE / ATTN_ERR_NULL. */
+int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal,
+                 int* b_out, int* h_out, int* m_out);
+
+/* Number of workgroups a dense launch uses, and query rows per tile. */
+int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* block_m_out);
+
+/* Human-readable text for a status code. */
+const char* attn_strerror(int code);
+
+/* Frees the library's fp8 workspace on every device that has one. */
+void attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

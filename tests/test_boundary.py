@@ -1,0 +1,112 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry
+point the header declares, rejects bad arguments before touching the device,
+and its tile scheduler is a bijection with the documented order."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_75_amd as ea
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ea.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return ea.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert {"attn_fwd", "attn_fp8_prepass", "attn_fwd_fp8", "attn_strerror", "attn_release"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=256, Sk=256, d=64,
+             scale=0.125, causal=0, cu=None, dtype=0)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                        a["Sk"], a["d"], a["scale"], a["causal"], a["cu"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(v=None), -1),
+    (dict(B=0), -2), (dict(Sq=0), -2), (dict(Sk=-3), -2), (dict(Hq=0), -2),
+    (dict(cu=FAKE, Sk=255), -2),
+    (dict(d=96), -3), (dict(d=256), -3),
+    (dict(Hq=6, Hkv=4), -4),
+    (dict(dtype=7), -5), (dict(dtype=-1), -5),
+    (dict(scale=float("nan")), -6), (dict(scale=float("inf")), -6), (dict(scale=0.0), -6),
+    (dict(scale=-0.1), -6),
+    (dict(dtype=2, cu=FAKE), -6),
+    (dict(dtype=2, d=64), -3),
+    (dict(Sq=1 << 30, Hq=64, d=128, Hkv=64), -9),
+])
+def test_validation_errors(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.attn_strerror(code)
+
+
+def test_other_entry_points_validate(lib):
+    assert lib.attn_fp8_prepass(None, FAKE, FAKE, 1, 128, 1, 128, 0, None, None) == -1
+    assert lib.attn_fp8_prepass(FAKE, FAKE, FAKE, 1, 128, 1, 64, 0, None, None) == -3
+    assert lib.attn_fp8_prepass(FAKE, FAKE, FAKE, 1, 0, 1, 128, 0, None, None) == -2
+    assert lib.attn_fwd_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 1, 128, 128, 128,
+                            0.1, 0, None) == -1
+    assert lib.attn_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 1, 128, 128, 64,
+                            0.1, 0, None) == -3
+    assert lib.attn_strerror(12345) == b"unknown status code"
+
+
+def test_default_signs_match_generator(lib):
+    assert ea.default_signs(128) == W.hadamard_signs(128, 55).tolist()
+
+
+def tiles(B, Hq, Hkv, Sq, causal, bm=128):
+    nM = (Sq + bm - 1) // bm
+    return [ea.tile_of(p, B, Hq, Hkv, Sq, bm, causal) for p in range(B * Hq * nM)], nM
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 256), (4, 16, 16, 2048), (2, 32, 8, 1024), (3, 6, 2, 300),
+                                   (1, 8, 1, 129)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_tile_map_is_bijection(lib, shape, causal):
+    B, Hq, Hkv, Sq = shape
+    ts, nM = tiles(B, Hq, Hkv, Sq, causal)
+    assert sorted(ts) == sorted((b, h, m) for b in range(B) for h in range(Hq) for m in range(nM))
+
+
+def test_tile_map_lpt_and_xcd_affinity(lib):
+    B, Hq, Hkv, Sq = 2, 32, 8, 2048       # 16 KV groups: 2 per XCD
+    ts, nM = tiles(B, Hq, Hkv, Sq, 1)
+    group = Hq // Hkv
+    for x in range(8):
+        mine = ts[x::8]                    # workgroups dispatched to XCD x
+        ms = [m for _, _, m in mine]
+        assert ms == sorted(ms, reverse=True)          # longest (latest) query blocks first
+        kv = {(b, h // group) for b, h, _ in mine}
+        assert len(kv) == 2                            # whole KV groups per XCD
+    # without even XCD split the order is still longest-first globally
+    ts, _ = tiles(1, 3, 1, 1024, 1)
+    ms = [m for _, _, m in ts]
+    assert ms == sorted(ms, reverse=True)
+
+
+def test_tile_of_rejects_bad_args(lib):
+    with pytest.raises(ea.AttnError):
+        ea.tile_of(10**6, 1, 2, 2, 256, 128, False)
+    with pytest.raises(ea.AttnError):
+        ea.tile_of(0, 1, 3, 2, 256, 128, False)

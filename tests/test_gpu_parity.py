@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (bf16/fp16): O max-abs <= 1e-2 and relative RMS <= 5e-3, LSE
+abs <= 1e-3.  Small shapes are compared element by element in full; the
+full-size workloads are compared on sampled (batch, head, row) sets that the
+oracle computes row by row, chosen to cover the first and last query blocks,
+ragged tails, every KV group and both lane halves of the tiles.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+O_MAXABS, O_RELRMS, LSE_ABS = 1e-2, 5e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_75_amd as m
+    m.library()
+    return m
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, tag=""):
+    o = o_gpu.detach().float().cpu().double().numpy()
+    l = lse_gpu.detach().cpu().double().numpy()
+    mask = ~np.isnan(o_ref)
+    assert mask.any()
+    diff = np.abs(o[mask] - o_ref[mask])
+    maxabs = float(diff.max())
+    relrms = float(np.sqrt((diff ** 2).sum() / (o_ref[mask] ** 2).sum()))
+    lm = ~np.isnan(lse_ref)
+    both_inf = np.isneginf(l[lm]) & np.isneginf(lse_ref[lm])
+    ldiff = np.where(both_inf, 0.0, np.abs(l[lm] - lse_ref[lm]))
+    lmax = float(ldiff.max())
+    print(f"[parity] {tag} O max-abs {maxabs:.3e} rel-RMS {relrms:.3e} LSE max-abs {lmax:.3e}", flush=True)
+    assert maxabs <= O_MAXABS, (tag, maxabs)
+    assert relrms <= O_RELRMS, (tag, relrms)
+    assert lmax <= LSE_ABS, (tag, lmax)
+
+
+def run_dense(ea, q, k, v, causal, scale=None):
+    o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------- small full comparisons
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 333, 333, 4, 2), (1, 128, 128, 2, 2), (1, 77, 200, 3, 1),
+                                   (1, 300, 65, 8, 2)])
+def test_small_full(ea, dtype, d, causal, shape):
+    B, Sq, Sk, Hq, Hkv = shape
+    print(f"[case] small dtype={dtype} d={d} causal={causal} shape={shape}", flush=True)
+    q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, dtype, seed=hash((B, Sq, Sk, d)) % 10000)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_dense(ea, q, k, v, causal)
+    o_ref, l_ref = A.attention(q, k, v, scale, causal)
+    compare(o, lse, o_ref, l_ref, f"small {dtype} d{d} c{int(causal)} {shape}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_degenerate_shapes(ea, d):
+    for (B, Sq, Sk, Hq, Hkv, causal) in [(1, 1, 1, 1, 1, False), (1, 1, 500, 2, 1, False),
+                                         (1, 1, 500, 2, 1, True), (2, 130, 1, 2, 2, False),
+                                         (1, 64, 64, 1, 1, True), (1, 129, 129, 4, 4, True)]:
+        print(f"[case] degenerate d={d} {(B, Sq, Sk, Hq, Hkv, causal)}", flush=True)
+        q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, "bf16", seed=7)
+        o, lse = run_dense(ea, q, k, v, causal)
+        o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
+        compare(o, lse, o_ref, l_ref, f"degenerate {(B, Sq, Sk, Hq, Hkv, causal)}")
+
+
+def test_single_key_and_identical_rows_exact(ea):
+    # single key: O = V0 exactly after rounding; identical V rows: O = v exactly
+    q, k, v = W.make_dense(1, 200, 1, 2, 2, 128, "bf16", seed=3)
+    o, lse = run_dense(ea, q, k, v, False)
+    assert torch.equal(o.cpu(), v.expand(1, 200, 2, 128))
+    q, k, v = W.make_dense(1, 300, 300, 2, 1, 64, "bf16", seed=4)
+    v = v[:, :1].expand(1, 300, 1, 64).contiguous()
+    for causal in (False, True):
+        o, _ = run_dense(ea, q, k, v, causal)
+        assert torch.equal(o.cpu(), v[:, :1].expand(1, 300, 2, 64))
+
+
+def test_zero_q_gives_log_n(ea):
+    q = torch.zeros(1, 300, 2, 128, dtype=torch.bfloat16)
+    _, k, v = W.make_dense(1, 300, 300, 2, 2, 128, "bf16", seed=5)
+    for causal in (False, True):
+        o, lse = run_dense(ea, q, k, v, causal)
+        n = np.arange(1, 301) if causal else np.full(300, 300)
+        np.testing.assert_allclose(lse.cpu().numpy()[0], np.log(n)[None, :].repeat(2, 0), atol=1e-5)
+        vm = v.double()
+        ref = (vm.cumsum(1) / torch.arange(1, 301).view(1, -1, 1, 1)) if causal else vm.mean(1, keepdim=True)
+        np.testing.assert_allclose(o.cpu().double().numpy(), ref.expand(1, 300, 2, 128).numpy(), atol=1e-2)
+
+
+def test_scale_other_than_default(ea):
+    q, k, v = W.make_dense(1, 200, 200, 2, 2, 64, "fp16", seed=8)
+    o, lse = run_dense(ea, q, k, v, True, scale=0.3)
+    o_ref, l_ref = A.attention(q, k, v, 0.3, True)
+    compare(o, lse, o_ref, l_ref, "scale 0.3")
+
+
+def test_deterministic(ea):
+    q, k, v = W.make_dense(2, 1000, 1000, 4, 2, 128, "bf16", seed=9)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = ea.fwd(qc, kc, vc, causal=True)
+    o2, l2 = ea.fwd(qc, kc, vc, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- varlen
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_small(ea, dtype, d):
+    lengths = [5, 0, 130, 1, 257, 64, 200]
+    print(f"[case] varlen small {dtype} d={d}", flush=True)
+    q, k, v, cu = W.make_varlen(lengths, 4, 2, d, dtype, seed=11)
+    for causal in (False, True):
+        o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                        cu_seqlens=torch.from_numpy(cu).cuda())
+        torch.cuda.synchronize()
+        o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal, cu_seqlens=cu)
+        compare(o, lse, o_ref, l_ref, f"varlen {dtype} d{d} c{int(causal)}")
+
+
+# ---------------------------------------------------------------- the five workloads
+def sampled_rows(S, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, S // 2, S - 129, S - 65, S - 33, S - 2, S - 1]
+    rows = set(r for r in fixed if 0 <= r < S) | set(rng.integers(0, S, n).tolist())
+    return np.array(sorted(rows))
+
+
+def test_c1(ea):
+    w = W.CONFIGS["c1"]
+    inp = W.make_inputs(w)
+    o, lse = run_dense(ea, inp["q"], inp["k"], inp["v"], w.causal)
+    o_ref, l_ref = A.attention(inp["q"], inp["k"], inp["v"], w.scale, w.causal)
+    compare(o, lse, o_ref, l_ref, "c1 full")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_dense_workload_sampled(ea, name):
+    w = W.CONFIGS[name]
+    print(f"[case] {name} full size, sampled rows", flush=True)
+    inp = W.make_inputs(w)
+    o, lse = run_dense(ea, inp["q"], inp["k"], inp["v"], w.causal)
+    rows = sampled_rows(w.Sq)
+    group = w.Hq // w.Hkv
+    heads = sorted(set([0, w.Hq - 1] + [g * group + (g % group) for g in range(w.Hkv)]))
+    for b in range(w.B):
+        o_ref, l_ref = A.attention(inp["q"], inp["k"], inp["v"], w.scale, w.causal,
+                                   heads=heads, rows=rows, batches=[b])
+        compare(o[b:b + 1], lse[b:b + 1], o_ref[b:b + 1], l_ref[b:b + 1], f"{name} b{b} sampled")
+
+
+def test_c2_full_heads(ea):
+    # c2: every row of three heads compared in full
+    w = W.CONFIGS["c2"]
+    inp = W.make_inputs(w)
+    o, lse = run_dense(ea, inp["q"], inp["k"], inp["v"], w.causal)
+    for b, h in [(0, 0), (3, 15), (1, 7)]:
+        o_ref, l_ref = A.attention(inp["q"], inp["k"], inp["v"], w.scale, w.causal, heads=[h], batches=[b])
+        compare(o[b:b + 1, :, h:h + 1], lse[b:b + 1, h:h + 1], o_ref[b:b + 1, :, h:h + 1],
+                l_ref[b:b + 1, h:h + 1], f"c2 b{b} h{h} full")
+
+
+def test_c4_varlen(ea):
+    w = W.CONFIGS["c4"]
+    inp = W.make_inputs(w)
+    cu = inp["cu_seqlens"]
+    o, lse = ea.fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=True,
+                    cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    # all sequences, heads 0, 5 and 15 in full
+    for h in (0, 5, 15):
+        o_ref, l_ref = A.attention(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1],
+                                   w.scale, True, cu_seqlens=cu)
+        compare(o[:, h:h + 1], lse[h:h + 1], o_ref, l_ref, f"c4 head {h}")
