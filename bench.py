@@ -1,0 +1,235 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--extra]
+
+One step is one pass of the hot path over one batch of the workload: for the
+bf16/fp16 workloads one ``attn_fwd`` call; for the fp8 workloads the fp8
+prepass of Q, K and V plus the fp8 attention kernel.  Inputs are resident in
+device memory before the timed region.  The timed region is bracketed by
+``torch.cuda.synchronize()`` and measured with HIP events on the stream the
+kernels are launched on (torch's current stream, which the binding passes to
+the library).
+
+Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s: 4 * d FLOP per
+unmasked (query, key) pair, so causal work is counted once (the pages'
+4*B*H*N^2*D convention, which also counts masked pairs, is reported beside it
+as ``tflops_dense_convention``).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, fp8) and % of MFMA peak, 1×MI355X"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+KERNEL_SOURCES = {"bf16": "exact_attention_75_amd/csrc/attn_fwd.hip",
+                  "fp16": "exact_attention_75_amd/csrc/attn_fwd.hip",
+                  "fp8": "exact_attention_75_amd/csrc/attn_fp8.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run one device-to-device copy of this many MiB "
+                         "(a reference kernel of known traffic for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def kernel_hash(dtype: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(name: str, dtype: str, launches_per_step: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{dtype}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256_16") != kernel_hash(dtype):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def flops_of(w, lengths=None):
+    from oracle.attention import attention_flops  # counting rule only, no arithmetic of the path
+    if w.varlen:
+        return attention_flops(0, 0, w.d, w.causal, H=w.Hq, lengths=lengths)
+    return attention_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
+
+
+def dense_convention_flops(w):
+    return 4.0 * w.B * w.Hq * w.Sq * w.Sk * w.d if not w.varlen else None
+
+
+def make_step(ea, w, dev_inp):
+    import torch
+    q, k, v, cu = dev_inp["q"], dev_inp["k"], dev_inp["v"], dev_inp["cu"]
+    o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype, device=q.device)
+    if w.varlen:
+        lse = torch.empty((w.Hq, q.shape[0]), dtype=torch.float32, device=q.device)
+    else:
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=q.device)
+    L = ea.library()
+    dt = {"bf16": ea.ATTN_BF16, "fp16": ea.ATTN_FP16, "fp8": ea.ATTN_FP8_E4M3}[w.dtype]
+    B = (len(dev_inp["lengths"]) if w.varlen else w.B)
+    cu_ptr = cu.data_ptr() if cu is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, w.Hq, w.Hkv,
+            w.Sq, w.Sk, w.d, float(w.scale), int(w.causal), cu_ptr, dt, stream)
+
+    def step():
+        rc = L.attn_fwd(*args)
+        if rc != 0:
+            raise RuntimeError(f"attn_fwd failed: {L.attn_strerror(rc).decode()}")
+    return step
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)  # ms for `steps` steps
+
+
+def device_inputs(w):
+    import torch
+    import workloads as W
+    inp = W.make_inputs(w)
+    lengths = W.varlen_lengths(total=w.Sq) if w.varlen else None
+    d = {k: inp[k].cuda() for k in ("q", "k", "v")}
+    d["cu"] = torch.from_numpy(inp["cu_seqlens"]).cuda() if inp["cu_seqlens"] is not None else None
+    d["lengths"] = lengths
+    return inp, d
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the fp64 oracle on whole (batch, head) slices of the same inputs
+    until about ``budget_s`` seconds of CPU work, and scale to TFLOP/s with the
+    same algorithmic FLOP count as the GPU figure."""
+    import numpy as np
+    from oracle.attention import attention, attention_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    done_flops, t0 = 0.0, time.perf_counter()
+    heads = 0
+    if w.varlen:
+        import workloads as W
+        lengths = W.varlen_lengths(total=w.Sq)
+        cu = W.cu_seqlens_from_lengths(lengths)
+        for h in range(w.Hq):
+            attention(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1], w.scale, w.causal,
+                      cu_seqlens=cu)
+            done_flops += attention_flops(0, 0, w.d, w.causal, H=1, lengths=lengths)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{heads} of {w.Hq} heads, all {len(lengths)} sequences, fp64 numpy"
+    else:
+        total = w.B * w.Hq
+        for i in range(total):
+            b, h = divmod(i, w.Hq)
+            attention(inp["q"], inp["k"], inp["v"], w.scale, w.causal, heads=[h], batches=[b])
+            done_flops += attention_flops(w.Sq, w.Sk, w.d, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{heads} of {total} (batch, head) slices, all {w.Sq} rows each, fp64 numpy"
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in "
+                                   "the design notes but not implemented", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    import exact_attention_75_amd as ea
+    import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    ea.library()
+    w = W.CONFIGS[a.workload]
+    inp, dev = device_inputs(w)
+    step = make_step(ea, w, dev)
+    ms_total = time_steps(step, a.steps, a.warmup)
+    ms = ms_total / a.steps
+    flops = flops_of(w, dev["lengths"])
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = traffic_for(w.name, w.dtype, 1)
+    cfg = {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} Sk={w.Sk} d={w.d} "
+                       f"{w.dtype} {'causal' if w.causal else 'full'}{' varlen' if w.varlen else ''}",
+           "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d, "causal": w.causal,
+           "varlen": w.varlen, "algorithmic_flop_per_step": flops}
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), CPU generator)",
+        "config": cfg,
+        "pct_of_dense_mfma_peak": round(100 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    dc = dense_convention_flops(w)
+    if dc:
+        out["tflops_dense_convention"] = round(dc / (ms * 1e-3) / 1e12, 2)
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n * 4
+        del src, dst
+    if a.extra:
+        for name in ("c1", "c2", "c4"):
+            if name == a.workload:
+                continue
+            wx = W.CONFIGS[name]
+            _, dx = device_inputs(wx)
+            sx = make_step(ea, wx, dx)
+            n = 200 if name == "c1" else a.steps
+            msx = time_steps(sx, n, a.warmup) / n
+            fx = flops_of(wx, dx["lengths"])
+            print(f"[extra] {name} {msx * 1e3:.1f} us  {fx / (msx * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr)
+            out.setdefault("other_workloads", {})[name] = {"ms": round(msx, 5),
+                                                          "tflops": round(fx / (msx * 1e-3) / 1e12, 2)}
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ def hipcc() -> str:
 
 def common_flags():
     return [
-        "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+        "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
         # packed fp32 VALU ops stay off: the compiler must not form v_pk_* f32 ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -71,7 +71,22 @@ def build(jobs: int = 4, save_temps: str | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    check_kernels(LIB)
     return LIB
+
+
+EXPECTED_KERNELS = ("fwd_kernel",)
+
+
+def check_kernels(path: str) -> None:
+    """Fail if the linked library lacks the device code objects of the
+    kernels (a host pass that drops a kernel template leaves no error)."""
+    blob = open(path, "rb").read()
+    if f"amdgcn-amd-amdhsa--{ARCH}".encode() not in blob:
+        raise RuntimeError(f"{path}: no {ARCH} code object embedded")
+    for name in EXPECTED_KERNELS:
+        if blob.count(name.encode()) < 2:
+            raise RuntimeError(f"{path}: kernel {name} missing from the device code")
 
 
 if __name__ == "__main__":

@@ -47,6 +47,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "kernels.h"
 
 namespace attn {
@@ -59,22 +61,47 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no stride; out-of-range reads return zero.
+constexpr int kBufferFlags = 0x00020000;
+
 template <typename T>
 struct Mma;
 
 template <>
 struct Mma<__bf16> {
   typedef bf16x8 vec8;
+  typedef __bf16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Row-sum share of one 8-key chunk.  bf16 keeps 8 significant bits, so a
+  // sum of rounded probabilities can be off by 2^-9 relative (a 2e-3 error
+  // in LSE when one key dominates): the sum is taken over the fp32 values.
+  static constexpr bool kSumRounded = false;
+  static __device__ __forceinline__ float sum8(vec8, const float (&pf)[8], float acc) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += pf[e];
+    return acc;
   }
 };
 
 template <>
 struct Mma<_Float16> {
   typedef f16x8 vec8;
+  typedef _Float16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // fp16 keeps 11 significant bits: summing the rounded probabilities (two
+  // per v_dot2) errs by at most 2^-11 relative in l, i.e. < 5e-4 in LSE.
+  static constexpr bool kSumRounded = true;
+  static __device__ __forceinline__ float sum8(vec8 p, const float (&)[8], float acc) {
+    const vec2 one = __builtin_bit_cast(vec2, 0x3C003C00u);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
   }
 };
 
@@ -107,6 +134,46 @@ __device__ __forceinline__ float wave_half_swap(float x) {
   return __int_as_float(lane < 32 ? r[1] : r[0]);
 }
 
+// N direct-to-LDS copies of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// copy i writes LDS bytes [dst + 1024 i, dst + 1024 (i + 1)), lane L the 16
+// bytes at offset 16 L, fetched from base + off[i].  Reads at or past `bytes`
+// return zeros (the buffer range check).
+template <int N>
+__device__ __forceinline__ void copy_rows_to_lds(const void* base, uint32_t bytes, char* dst,
+                                                 const uint32_t (&off)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // (the buffer-resource type exists only in the device pass of the compiler)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + i * 1024), 16, off[i], 0, 0, 0);
+#endif
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) issued as inline assembly: the
+// compiler does not see it as an LDS access, so it does not make it wait for
+// the K/V copies of the next tile that are still in flight.  The caller waits
+// for the result with lds_wait().
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_tr16(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(i16x4 (&r)[N]) {
+  if constexpr (N == 8) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                   "+v"(r[7]));
+  } else {
+    static_assert(N == 4, "");
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+  }
+}
+
 template <typename T, int D, int BN, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
@@ -118,14 +185,15 @@ fwd_kernel(FwdParams p) {
   constexpr int NB = BN / 32;          // 32-key blocks per tile
   constexpr int NC = BN / 16;          // 16-key chunks per tile (second GEMM)
   constexpr int DB = D / 32;           // 32-column blocks of O^T
-  constexpr int ROW_BYTES = D * 2;
-  constexpr int TILE_BYTES = BN * ROW_BYTES;
-  constexpr int LOADS = BN * CPR / (NW * 64);   // DMA instructions per wave per tensor
+  constexpr int ROW = D * 2;           // bytes per K/V row in LDS
+  constexpr int TILE = BN * ROW;       // bytes per K or V tile
+  constexpr int LOADS = BN * CPR / (NW * 64);   // DMA instructions per wave per tile
   constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
   constexpr float NEG_INF = -__builtin_inff();
-  static_assert(BN % 32 == 0 && (BN * CPR) % (NW * 64) == 0, "tile shape");
+  static_assert(BN == 64 && (BN * CPR) % (NW * 64) == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];  // [stage][K, V]
+  // [K stage 0 | K stage 1 | V stage 0 | V stage 1]
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,73 +258,136 @@ fwd_kernel(FwdParams p) {
   }
 
   // ---------------------------------------------------------------- K/V copy
-  auto issue_tile = [&](int t, int stage) {
-    const int j0 = t * BN;
+  // buffer_load ... lds: one instruction writes 64 consecutive 16-byte LDS
+  // chunks, lane L fetching the global chunk that belongs at position L under
+  // the swizzle.  The per-lane byte offsets relative to the tile's first row
+  // are tile-invariant (computed once); each tile gets a buffer resource whose
+  // base is its first row and whose size ends at the sequence end, so the
+  // hardware range check returns zeros for the rows past the end of a ragged
+  // last tile (their scores are masked and their P is 0).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kdma[LOADS], vdma[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int blk = wave * LOADS + i;           // 64-chunk block written by this instruction
-      const int pos = blk * 64 + lane;            // LDS chunk position (lane-linear)
-      const int row = pos / CPR;
-      const int phys = pos % CPR;
-      const int grow = (j0 + row < kv_len) ? j0 + row : kv_len - 1;
-      const T* ksrc = Kp + (long long)grow * ks + ((phys ^ swz_k<D>(row)) * 8);
-      const T* vsrc = Vp + (long long)grow * ks + ((phys ^ swz_v<D>(row)) * 8);
-      __builtin_amdgcn_global_load_lds((const void*)ksrc, (LDS_AS void*)(smem[stage][0] + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vsrc, (LDS_AS void*)(smem[stage][1] + blk * 1024), 16, 0, 0);
-    }
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = (wave_u * LOADS + i) * 64 + lane;
+    const int row = pos / CPR, phys = pos % CPR;
+    kdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_k<D>(row)) << 4));
+    vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+  }
+  auto issue = [&](const T* src, int t, char* dst, bool is_v) {
+    const int j0 = t * BN;
+    const uint32_t bytes = (uint32_t)(kv_len - j0) * (uint32_t)ks * 2u;
+    copy_rows_to_lds<LOADS>((const void*)(src + (long long)j0 * ks), bytes, dst + wave_u * LOADS * 1024,
+                            is_v ? vdma : kdma);
   };
+
+  // per-lane LDS byte offsets, invariant over tiles
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+  int koff[KT];
+  {
+    const int r = key_perm(l32);          // block bb adds 32 rows: an immediate offset
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) koff[kk] = r * ROW + (((2 * kk + h) ^ swz_k<D>(r)) << 4);
+  }
+  uint32_t voff[DB];
+  {
+    const int G = lane >> 4, i16 = lane & 15;
+    const int r = 8 * h + (i16 >> 2);     // chunk cc adds 16 rows, the second read 4 rows
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dd = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
+      voff[db] = lds0 + 2 * TILE + r * ROW + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
+    }
+  }
 
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  // P of the previous tile.  Before the first tile it is zero and the V stage
+  // it pairs with (stage 1) is zero-filled, so the first tile runs the same
+  // interleaved code as every other tile and adds exactly zero to O.
+  vec8 pprev[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) pprev[cc] = vec8{};
+  {
+    // both V stages start as zeros (stage 1 pairs with the zero P above; a
+    // ragged tile leaves zeros, never stale bit patterns, in unused rows)
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    i32x4* z = (i32x4*)(smem + 2 * TILE);
+#pragma unroll
+    for (int i = tid; i < 2 * TILE / 16; i += kThreads) z[i] = i32x4{};
+  }
   float m_run = NEG_INF;   // running max of scale*log2(e)*s for query l32 (same in both halves)
   float l_run = 0.f;       // this lane half's share of the running sum
+  bool has_prev = false;   // pprev holds P of a computed tile not yet multiplied into O
+  float alpha_pend = 1.f;  // rescale of O owed before the next P V product
   const float c = p.scale_log2;
   const int qi = qw + l32;
 
-  // per-lane LDS addressing, invariant over tiles
-  int k_off[KT][NB];
-#pragma unroll
-  for (int kk = 0; kk < KT; ++kk)
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int r = 32 * bb + key_perm(l32);
-      k_off[kk][bb] = r * ROW_BYTES + (((2 * kk + h) ^ swz_k<D>(r)) << 4);
-    }
-  const int G = lane >> 4, i16 = lane & 15;
-  int v_off[NC][DB];
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc)
+  // O^T += V^T P^T for one 16-key chunk; V tile at byte offset vbase
+  auto pv_chunk = [&](i16x4 (&vr)[2 * DB], const vec8& pc) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int r = 16 * cc + 8 * h + (i16 >> 2);
-      const int dd = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
-      v_off[cc][db] = r * ROW_BYTES + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
+      const i16x8 w = __builtin_shufflevector(vr[2 * db], vr[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = Mma<T>::run(__builtin_bit_cast(vec8, w), pc, o[db]);
     }
+  };
+  auto read_v = [&](i16x4 (&vr)[2 * DB], uint32_t vstage, auto cc_tag) {
+    constexpr int CC = decltype(cc_tag)::value;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      vr[2 * db] = lds_tr16<CC * 16 * ROW>(voff[db] + vstage);
+      vr[2 * db + 1] = lds_tr16<CC * 16 * ROW + 4 * ROW>(voff[db] + vstage);
+    }
+  };
 
-  if (ntile > 0) issue_tile(0, 0);
+  if (ntile > 0) issue(Kp, 0, smem, false);
 
-  for (int t = 0; t < ntile; ++t) {
+  for (int t = 0; t <= ntile; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntile) issue_tile(t + 1, (t + 1) & 1);
+    if (t + 1 < ntile) issue(Kp, t + 1, smem + ((t + 1) & 1) * TILE, false);
+    if (t < ntile) issue(Vp, t, smem + 2 * TILE + (t & 1) * TILE, true);
     const int j0 = t * BN;
-    if (CAUSAL && j0 > qw + 31) continue;   // tile entirely above this wave's diagonal
+    const bool cur = (t < ntile) && !(CAUSAL && j0 > qw + 31);
+    const uint32_t vprev = ((t + 1) & 1) * TILE;   // V of tile t-1
 
-    const char* Ks = smem[t & 1][0];
-    const char* Vs = smem[t & 1][1];
+    // O picks up the rescale of the previous tile's max before P_{t-1} V_{t-1}
+    // is added (kept out of the interleaved block below: it is a rare branch)
+    if (__builtin_amdgcn_ballot_w64(alpha_pend != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha_pend;
+    }
+    alpha_pend = 1.f;
 
-    // ---- S^T = K Q^T
+    if (!cur) {
+      if (has_prev) {
+        // ---- last tile of this wave: O^T += V^T P^T only
+        [&]<int... CC>(std::integer_sequence<int, CC...>) {
+          ([&] {
+            i16x4 vr[2 * DB];
+            read_v(vr, vprev, std::integral_constant<int, CC>{});
+            lds_wait(vr);
+            pv_chunk(vr, pprev[CC]);
+          }(), ...);
+        }(std::make_integer_sequence<int, NC>{});
+        has_prev = false;
+      }
+      continue;
+    }
+
+    // ---- S^T = K Q^T (block 0 first so its max can start under block 1)
+    const char* Ks = smem + (t & 1) * TILE;
     f32x16 s[NB];
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) s[bb] = f32x16{};
+    for (int bb = 0; bb < NB; ++bb) {
+      s[bb] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KT; ++kk)
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const vec8 a = *(const vec8*)(Ks + k_off[kk][bb]);
+      for (int kk = 0; kk < KT; ++kk) {
+        const vec8 a = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
         s[bb] = Mma<T>::run(a, qf[kk], s[bb]);
       }
+    }
 
     // ---- mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
     const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
@@ -278,39 +409,43 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
     mx = fmaxf(mx, wave_half_swap(mx));
+    // lazy rescale, decided for the whole wave and kept branch-free so that
+    // the exponentials below stay in one basic block with the MFMAs
     const float m_new = fmaxf(m_run, mx * c);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
-      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
+    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0;
+    const float m_upd = moved ? m_new : m_run;
+    const float alpha = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
+    m_run = m_upd;
     const float msub = (m_run == NEG_INF) ? 0.f : m_run;
 
-    // ---- P = exp2(c*s - m), row sum, convert to the operand type
-    vec8 pk[NC];
+    // ---- P = exp2(c*s - m) for chunk cc, with its row-sum share
+    vec8 pcur[NC];
     float rs = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+    auto softmax_chunk = [&](int cc) {
+      float pf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + e], c, -msub));
-        rs += pe;
-        pk[cc][e] = (T)pe;
+        pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + e], c, -msub));
+        pcur[cc][e] = (T)pf[e];
       }
-    l_run += rs;
+      rs = Mma<T>::sum8(pcur[cc], pf, rs);
+    };
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T of the previous tile, interleaved with this tile's exp
+    [&]<int... CC>(std::integer_sequence<int, CC...>) {
+      ([&] {
+        i16x4 vr[2 * DB];
+        read_v(vr, vprev, std::integral_constant<int, CC>{});
+        softmax_chunk(CC);
+        lds_wait(vr);
+        pv_chunk(vr, pprev[CC]);
+      }(), ...);
+    }(std::make_integer_sequence<int, NC>{});
+    l_run = l_run * alpha + rs;
+    alpha_pend = alpha;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Vs + v_off[cc][db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Vs + v_off[cc][db] + 4 * ROW_BYTES));
-        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = Mma<T>::run(__builtin_bit_cast(vec8, w), pk[cc], o[db]);
-      }
+    for (int cc = 0; cc < NC; ++cc) pprev[cc] = pcur[cc];
+    has_prev = true;
   }
 
   // ---------------------------------------------------------------- epilogue
