@@ -197,7 +197,7 @@ fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -265,7 +265,7 @@ fwd_kernel(FwdParams p) {
   // base is its first row and whose size ends at the sequence end, so the
   // hardware range check returns zeros for the rows past the end of a ragged
   // last tile (their scores are masked and their P is 0).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wave_u = wave;
   uint32_t kdma[LOADS], vdma[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -306,9 +306,9 @@ fwd_kernel(FwdParams p) {
   // P of the previous tile.  Before the first tile it is zero and the V stage
   // it pairs with (stage 1) is zero-filled, so the first tile runs the same
   // interleaved code as every other tile and adds exactly zero to O.
-  vec8 pprev[NC];
+  vec8 pA[NC], pB[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) pprev[cc] = vec8{};
+  for (int cc = 0; cc < NC; ++cc) pA[cc] = vec8{};
   {
     // both V stages start as zeros (stage 1 pairs with the zero P above; a
     // ragged tile leaves zeros, never stale bit patterns, in unused rows)
@@ -319,7 +319,6 @@ fwd_kernel(FwdParams p) {
   }
   float m_run = NEG_INF;   // running max of scale*log2(e)*s for query l32 (same in both halves)
   float l_run = 0.f;       // this lane half's share of the running sum
-  bool has_prev = false;   // pprev holds P of a computed tile not yet multiplied into O
   float alpha_pend = 1.f;  // rescale of O owed before the next P V product
   const float c = p.scale_log2;
   const int qi = qw + l32;
@@ -343,49 +342,61 @@ fwd_kernel(FwdParams p) {
 
   if (ntile > 0) issue(Kp, 0, smem, false);
 
-  for (int t = 0; t <= ntile; ++t) {
+  // Per tile t the workgroup waits for K_t and V_{t-1}, then starts the copies
+  // of K_{t+1} and V_t into the buffers freed by tile t-1.  Every wave takes
+  // part in all ntile + 1 of these rounds; a wave of a causal block stops
+  // computing after its last tile below the diagonal.
+  auto top = [&](int t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 1 < ntile) issue(Kp, t + 1, smem + ((t + 1) & 1) * TILE, false);
     if (t < ntile) issue(Vp, t, smem + 2 * TILE + (t & 1) * TILE, true);
-    const int j0 = t * BN;
-    const bool cur = (t < ntile) && !(CAUSAL && j0 > qw + 31);
-    const uint32_t vprev = ((t + 1) & 1) * TILE;   // V of tile t-1
-
-    // O picks up the rescale of the previous tile's max before P_{t-1} V_{t-1}
-    // is added (kept out of the interleaved block below: it is a rare branch)
+  };
+  // O picks up the rescale owed for the previous tile's max before the next
+  // P V product (a rare, wave-uniform branch)
+  auto settle_alpha = [&] {
     if (__builtin_amdgcn_ballot_w64(alpha_pend != 1.f) != 0) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha_pend;
     }
     alpha_pend = 1.f;
+  };
 
-    if (!cur) {
-      if (has_prev) {
-        // ---- last tile of this wave: O^T += V^T P^T only
-        [&]<int... CC>(std::integer_sequence<int, CC...>) {
-          ([&] {
-            i16x4 vr[2 * DB];
-            read_v(vr, vprev, std::integral_constant<int, CC>{});
-            lds_wait(vr);
-            pv_chunk(vr, pprev[CC]);
-          }(), ...);
-        }(std::make_integer_sequence<int, NC>{});
-        has_prev = false;
-      }
-      continue;
-    }
+  // Full step: S_t = K_t Q^T, softmax of tile t into pout, and P_{t-1} V_{t-1}
+  // (pin) into O, interleaved with the exponentials.  Unrolled by two below so
+  // that the two P register sets swap roles instead of being copied.
+  auto step_full = [&](int t, vec8 (&pin)[NC], vec8 (&pout)[NC]) {
+    top(t);
+    settle_alpha();
+    const int j0 = t * BN;
+    const uint32_t vprev = ((t + 1) & 1) * TILE;   // V of tile t-1
 
-    // ---- S^T = K Q^T (block 0 first so its max can start under block 1)
+    // ---- S^T = K Q^T.  k-step outer so that each pair of LDS reads feeds two
+    // independent accumulators, with the reads issued two k-steps ahead of
+    // their MFMAs to cover the LDS latency.
     const char* Ks = smem + (t & 1) * TILE;
     f32x16 s[NB];
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      s[bb] = f32x16{};
+    for (int bb = 0; bb < NB; ++bb) s[bb] = f32x16{};
+    {
+      constexpr int AHEAD = 2;
+      vec8 kr[AHEAD + 1][NB];
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) kr[kk][bb] = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
 #pragma unroll
       for (int kk = 0; kk < KT; ++kk) {
-        const vec8 a = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
-        s[bb] = Mma<T>::run(a, qf[kk], s[bb]);
+        if (kk + AHEAD < KT) {
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb)
+            kr[(kk + AHEAD) % (AHEAD + 1)][bb] = *(const vec8*)(Ks + koff[kk + AHEAD] + bb * 32 * ROW);
+        }
+        // keep the reads ahead of the MFMAs (the scheduler would otherwise
+        // sink them next to their use to save registers)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) s[bb] = Mma<T>::run(kr[kk % (AHEAD + 1)][bb], qf[kk], s[bb]);
       }
     }
 
@@ -419,16 +430,15 @@ fwd_kernel(FwdParams p) {
     const float msub = (m_run == NEG_INF) ? 0.f : m_run;
 
     // ---- P = exp2(c*s - m) for chunk cc, with its row-sum share
-    vec8 pcur[NC];
     float rs = 0.f;
     auto softmax_chunk = [&](int cc) {
       float pf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + e], c, -msub));
-        pcur[cc][e] = (T)pf[e];
+        pout[cc][e] = (T)pf[e];
       }
-      rs = Mma<T>::sum8(pcur[cc], pf, rs);
+      rs = Mma<T>::sum8(pout[cc], pf, rs);
     };
 
     // ---- O^T += V^T P^T of the previous tile, interleaved with this tile's exp
@@ -438,15 +448,44 @@ fwd_kernel(FwdParams p) {
         read_v(vr, vprev, std::integral_constant<int, CC>{});
         softmax_chunk(CC);
         lds_wait(vr);
-        pv_chunk(vr, pprev[CC]);
+        pv_chunk(vr, pin[CC]);
       }(), ...);
     }(std::make_integer_sequence<int, NC>{});
     l_run = l_run * alpha + rs;
     alpha_pend = alpha;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) pprev[cc] = pcur[cc];
-    has_prev = true;
+  };
+
+  // Closing step of a wave: the last P V product only.
+  auto step_pv = [&](int t, vec8 (&pin)[NC]) {
+    top(t);
+    settle_alpha();
+    const uint32_t vprev = ((t + 1) & 1) * TILE;
+    [&]<int... CC>(std::integer_sequence<int, CC...>) {
+      ([&] {
+        i16x4 vr[2 * DB];
+        read_v(vr, vprev, std::integral_constant<int, CC>{});
+        lds_wait(vr);
+        pv_chunk(vr, pin[CC]);
+      }(), ...);
+    }(std::make_integer_sequence<int, NC>{});
+  };
+
+  // tiles this wave computes (a causal wave stops at its diagonal)
+  const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
+  int t = 0;
+  for (; t + 1 < n_w; t += 2) {
+    step_full(t, pA, pB);
+    step_full(t + 1, pB, pA);
   }
+  if (t < n_w) {
+    step_full(t, pA, pB);
+    step_pv(t + 1, pB);
+    t += 2;
+  } else {
+    step_pv(t, pA);
+    t += 1;
+  }
+  for (; t <= ntile; ++t) top(t);
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + wave_half_swap(l_run);
