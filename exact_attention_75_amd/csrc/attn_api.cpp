@@ -32,7 +32,7 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
   if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_ARG;
   // per-tensor element counts and in-kernel 32-bit row offsets
   if ((long long)Sq * Hq * d > kMax32 || (long long)Sk * Hkv * d > kMax32) return ATTN_ERR_SIZE;
-  if ((long long)B * Hq * ((Sq + attn::kBlockM - 1) / attn::kBlockM) > kMax32) return ATTN_ERR_SIZE;
+  if ((long long)B * Hq * ((Sq + attn::kBlockMMin - 1) / attn::kBlockMMin) > kMax32) return ATTN_ERR_SIZE;
   return ATTN_OK;
 }
 
@@ -113,10 +113,10 @@ int attn_default_signs(float* signs_host, int n) {
 int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* block_m_out) {
   if (!grid_out || !block_m_out) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Sq <= 0) return ATTN_ERR_SHAPE;
-  (void)d;
-  (void)dtype;
-  *block_m_out = attn::kBlockM;
-  *grid_out = B * Hq * ((Sq + attn::kBlockM - 1) / attn::kBlockM);
+  if (dtype < ATTN_BF16 || dtype > ATTN_FP8_E4M3_HADAMARD) return ATTN_ERR_DTYPE;
+  const int bm = dtype >= ATTN_FP8_E4M3 ? attn::fwd_fp8_block_m() : attn::fwd_block_m(dtype, d, 0);
+  *block_m_out = bm;
+  *grid_out = B * Hq * ((Sq + bm - 1) / bm);
   return ATTN_OK;
 }
 
@@ -153,7 +153,7 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   p.Sk = Sk;
   p.group = Hq / Hkv;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBlockM, causal);
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_fp8_block_m(), causal);
   p.grid = p.tm.ntiles;
   hipError_t e = attn::launch_fwd_fp8(p, causal, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
@@ -261,11 +261,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (varlen) {
     // one tile per (head, query block of a sequence); the number of blocks is
     // at most ceil(T / BM) + (number of sequences), the rest exit at once
-    const long long nb = (Sq + attn::kBlockM - 1) / attn::kBlockM + B;
+    const int bm = attn::fwd_block_m(dtype, d, 1);
+    const long long nb = (Sq + bm - 1) / bm + B;
     if (nb * Hq > kMax32) return ATTN_ERR_SIZE;
     p.grid = (int)(nb * Hq);
   } else {
-    p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBlockM, causal);
+    p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_block_m(dtype, d, 0), causal);
     p.grid = p.tm.ntiles;
   }
   hipError_t e = attn::launch_fwd(p, dtype, d, causal, varlen ? 1 : 0, s);

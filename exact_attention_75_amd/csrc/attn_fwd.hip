@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <utility>
 
@@ -71,37 +72,16 @@ struct Mma;
 template <>
 struct Mma<__bf16> {
   typedef bf16x8 vec8;
-  typedef __bf16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // Row-sum share of one 8-key chunk.  bf16 keeps 8 significant bits, so a
-  // sum of rounded probabilities can be off by 2^-9 relative (a 2e-3 error
-  // in LSE when one key dominates): the sum is taken over the fp32 values.
-  static constexpr bool kSumRounded = false;
-  static __device__ __forceinline__ float sum8(vec8, const float (&pf)[8], float acc) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += pf[e];
-    return acc;
   }
 };
 
 template <>
 struct Mma<_Float16> {
   typedef f16x8 vec8;
-  typedef _Float16 vec2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  // fp16 keeps 11 significant bits: summing the rounded probabilities (two
-  // per v_dot2) errs by at most 2^-11 relative in l, i.e. < 5e-4 in LSE.
-  static constexpr bool kSumRounded = true;
-  static __device__ __forceinline__ float sum8(vec8 p, const float (&)[8], float acc) {
-    const vec2 one = __builtin_bit_cast(vec2, 0x3C003C00u);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
-    return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
   }
 };
 
@@ -151,6 +131,15 @@ __device__ __forceinline__ void copy_rows_to_lds(const void* base, uint32_t byte
 #endif
 }
 
+// Empty uses that pin a computed value at this point of the program: without
+// them the compiler sinks the exponentials of one MFMA stretch down to their
+// first use in a later stretch, undoing the interleave.
+__device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
+template <typename V>
+__device__ __forceinline__ void keep_vec(const V& x) {
+  asm volatile("" ::"v"(x));
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16) issued as inline assembly: the
 // compiler does not see it as an LDS access, so it does not make it wait for
 // the K/V copies of the next tile that are still in flight.  The caller waits
@@ -162,24 +151,32 @@ __device__ __forceinline__ i16x4 lds_tr16(uint32_t addr) {
   return r;
 }
 
-template <int N>
+// Wait until at most LEFT LDS operations are outstanding, then consider r
+// valid.  LDS operations complete in order, so with LEFT = the number of LDS
+// reads issued after r's, r is complete.
+template <int LEFT, int N>
 __device__ __forceinline__ void lds_wait(i16x4 (&r)[N]) {
   if constexpr (N == 8) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
+    asm volatile("s_waitcnt lgkmcnt(%8)"
                  : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                   "+v"(r[7]));
+                   "+v"(r[7])
+                 : "n"(LEFT));
   } else {
     static_assert(N == 4, "");
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(LEFT));
   }
 }
 
-template <typename T, int D, int BN, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup, each owning 32 query rows.  NW == 4: two
+// workgroups share a CU and their waves interleave freely.  NW == 8: one
+// workgroup per CU, two waves per SIMD (wave w and w + 4), run as two groups
+// offset by half a tile (ping-pong, below).
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
-  constexpr int NW = 4;
-  constexpr int BM = kBlockM;
+  constexpr int NTHREADS = 64 * NW;
+  constexpr int BM = 32 * NW;
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int KT = D / 16;           // k-steps of the first GEMM
   constexpr int NB = BN / 32;          // 32-key blocks per tile
@@ -192,14 +189,22 @@ fwd_kernel(FwdParams p) {
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(BN == 64 && (BN * CPR) % (NW * 64) == 0, "tile shape");
 
-  // [K stage 0 | K stage 1 | V stage 0 | V stage 1]
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  // With d = 128 the Q block lives in LDS (its 32 registers per lane are
+  // needed by the pipeline); with d = 64 it stays in registers.
+  constexpr bool QLDS = (D == 128);
+  // [K stage 0 | K stage 1 | V stage 0 | V stage 1 | Q block (QLDS)]
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const qsm = smem + 4 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int h = lane >> 5;
   const int l32 = lane & 31;
+  // Query row (within the wave's 32) of this lane's MFMA column.  Columns may
+  // be assigned to queries in any fixed order; using the same permutation as
+  // the key rows lets Q and K share their LDS read offsets.
+  const int qlane = key_perm(l32);
 
   // ---------------------------------------------------------------- tile decode
   int b, hq, mblk, q_len, kv_len;
@@ -248,10 +253,12 @@ fwd_kernel(FwdParams p) {
   const int ntile = (kv_end + BN - 1) / BN;
 
   // ---------------------------------------------------------------- Q fragment
-  // B operand of S^T = K Q^T: lane holds query l32, head-dim 16*kk + 8*h .. +7.
-  vec8 qf[KT];
-  {
-    const int qrow = (qw + l32 < q_len) ? qw + l32 : q_len - 1;
+  // B operand of S^T = K Q^T: lane holds query qlane, head-dim 16*kk + 8*h
+  // .. +7.  In registers for d = 64; for d = 128 read from LDS per k-step.
+  constexpr int KTR = QLDS ? 1 : KT;
+  vec8 qf[KTR];
+  if constexpr (!QLDS) {
+    const int qrow = (qw + qlane < q_len) ? qw + qlane : q_len - 1;
     const T* qr = Qp + (long long)qrow * qs + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KT; ++kk) qf[kk] = *(const vec8*)(qr + 16 * kk);
@@ -281,11 +288,26 @@ fwd_kernel(FwdParams p) {
                             is_v ? vdma : kdma);
   };
 
+  if constexpr (QLDS) {
+    // the workgroup's BM query rows into LDS, K-style swizzle; rows past the
+    // end of the sequence read as zeros (buffer range check)
+    constexpr int QLOADS = BM * CPR / (NW * 64);
+    uint32_t qdma[QLOADS];
+#pragma unroll
+    for (int i = 0; i < QLOADS; ++i) {
+      const int pos = (wave * QLOADS + i) * 64 + lane;
+      const int row = pos / CPR, phys = pos % CPR;
+      qdma[i] = (uint32_t)(row * qs * 2 + ((phys ^ swz_k<D>(row)) << 4));
+    }
+    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
+    copy_rows_to_lds<QLOADS>((const void*)(Qp + (long long)q0 * qs), bytes, qsm + wave * QLOADS * 1024, qdma);
+  }
+
   // per-lane LDS byte offsets, invariant over tiles
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
   int koff[KT];
   {
-    const int r = key_perm(l32);          // block bb adds 32 rows: an immediate offset
+    const int r = qlane;                  // block bb adds 32 rows: an immediate offset
 #pragma unroll
     for (int kk = 0; kk < KT; ++kk) koff[kk] = r * ROW + (((2 * kk + h) ^ swz_k<D>(r)) << 4);
   }
@@ -303,34 +325,23 @@ fwd_kernel(FwdParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  // P of the previous tile.  Before the first tile it is zero and the V stage
-  // it pairs with (stage 1) is zero-filled, so the first tile runs the same
-  // interleaved code as every other tile and adds exactly zero to O.
-  vec8 pA[NC], pB[NC];
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc) pA[cc] = vec8{};
   {
-    // both V stages start as zeros (stage 1 pairs with the zero P above; a
-    // ragged tile leaves zeros, never stale bit patterns, in unused rows)
+    // both V stages start as zeros, so that the rows past the end of a ragged
+    // tile hold zeros or earlier V data, never arbitrary bit patterns
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     i32x4* z = (i32x4*)(smem + 2 * TILE);
 #pragma unroll
-    for (int i = tid; i < 2 * TILE / 16; i += kThreads) z[i] = i32x4{};
+    for (int i = tid; i < 2 * TILE / 16; i += NTHREADS) z[i] = i32x4{};
   }
-  float m_run = NEG_INF;   // running max of scale*log2(e)*s for query l32 (same in both halves)
-  float l_run = 0.f;       // this lane half's share of the running sum
-  float alpha_pend = 1.f;  // rescale of O owed before the next P V product
+  float m_run = NEG_INF;   // running max of scale*log2(e)*s for the lane's query (same in both halves)
+  // This lane half's share of the running sum of P, taken over the fp32
+  // probabilities: bf16 keeps 8 significant bits, so summing the rounded
+  // values could be off by 2^-9 relative, a 2e-3 error in LSE.
+  float l_run = 0.f;
   const float c = p.scale_log2;
-  const int qi = qw + l32;
+  const int qi = qw + qlane;
+  const char* const qwave = qsm + wave * 32 * ROW;   // this wave's Q rows (QLDS)
 
-  // O^T += V^T P^T for one 16-key chunk; V tile at byte offset vbase
-  auto pv_chunk = [&](i16x4 (&vr)[2 * DB], const vec8& pc) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x8 w = __builtin_shufflevector(vr[2 * db], vr[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = Mma<T>::run(__builtin_bit_cast(vec8, w), pc, o[db]);
-    }
-  };
   auto read_v = [&](i16x4 (&vr)[2 * DB], uint32_t vstage, auto cc_tag) {
     constexpr int CC = decltype(cc_tag)::value;
 #pragma unroll
@@ -340,67 +351,33 @@ fwd_kernel(FwdParams p) {
     }
   };
 
-  if (ntile > 0) issue(Kp, 0, smem, false);
+  // Per-wave software pipeline.  MFMA and VALU work overlap well when one
+  // wave interleaves them, poorly when they come from different waves, so
+  // every stretch of MFMAs below carries its share of the softmax:
+  //   A: S_{t+1} = K_{t+1} Q^T (16 MFMA)   with  exp2 of S_t, chunks 0-1
+  //   B: P_t V_t, chunks 0-1 (8 MFMA)      with  exp2 of S_t, chunks 2-3
+  //   C: P_t V_t, chunks 2-3 (8 MFMA)      with  mask + row max of S_{t+1}
+  // The probabilities are computed in place over S_t and packed into P.
 
-  // Per tile t the workgroup waits for K_t and V_{t-1}, then starts the copies
-  // of K_{t+1} and V_t into the buffers freed by tile t-1.  Every wave takes
-  // part in all ntile + 1 of these rounds; a wave of a causal block stops
-  // computing after its last tile below the diagonal.
-  auto top = [&](int t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntile) issue(Kp, t + 1, smem + ((t + 1) & 1) * TILE, false);
-    if (t < ntile) issue(Vp, t, smem + 2 * TILE + (t & 1) * TILE, true);
-  };
-  // O picks up the rescale owed for the previous tile's max before the next
-  // P V product (a rare, wave-uniform branch)
-  auto settle_alpha = [&] {
-    if (__builtin_amdgcn_ballot_w64(alpha_pend != 1.f) != 0) {
+  // exp2(c*s - m) in place for elements [e0, e0+n) of 16-key chunk cc
+  auto exps = [&](f32x16 (&sc)[NB], float msub, int cc, int e0, int n, float& rs) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha_pend;
+    for (int e = e0; e < e0 + n; ++e) {
+      const int i = 8 * (cc & 1) + e;
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc >> 1][i], c, -msub));
+      sc[cc >> 1][i] = x;
+      rs += x;
+      keep(x);
     }
-    alpha_pend = 1.f;
   };
-
-  // Full step: S_t = K_t Q^T, softmax of tile t into pout, and P_{t-1} V_{t-1}
-  // (pin) into O, interleaved with the exponentials.  Unrolled by two below so
-  // that the two P register sets swap roles instead of being copied.
-  auto step_full = [&](int t, vec8 (&pin)[NC], vec8 (&pout)[NC]) {
-    top(t);
-    settle_alpha();
+  auto pack = [&](f32x16 (&sc)[NB], int cc, vec8 (&pc)[NC]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pc[cc][e] = (T)sc[cc >> 1][8 * (cc & 1) + e];
+    keep_vec(pc[cc]);
+  };
+  // mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
+  auto mask = [&](int t, f32x16 (&sn)[NB]) {
     const int j0 = t * BN;
-    const uint32_t vprev = ((t + 1) & 1) * TILE;   // V of tile t-1
-
-    // ---- S^T = K Q^T.  k-step outer so that each pair of LDS reads feeds two
-    // independent accumulators, with the reads issued two k-steps ahead of
-    // their MFMAs to cover the LDS latency.
-    const char* Ks = smem + (t & 1) * TILE;
-    f32x16 s[NB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) s[bb] = f32x16{};
-    {
-      constexpr int AHEAD = 2;
-      vec8 kr[AHEAD + 1][NB];
-#pragma unroll
-      for (int kk = 0; kk < AHEAD; ++kk)
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) kr[kk][bb] = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
-#pragma unroll
-      for (int kk = 0; kk < KT; ++kk) {
-        if (kk + AHEAD < KT) {
-#pragma unroll
-          for (int bb = 0; bb < NB; ++bb)
-            kr[(kk + AHEAD) % (AHEAD + 1)][bb] = *(const vec8*)(Ks + koff[kk + AHEAD] + bb * 32 * ROW);
-        }
-        // keep the reads ahead of the MFMAs (the scheduler would otherwise
-        // sink them next to their use to save registers)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) s[bb] = Mma<T>::run(kr[kk % (AHEAD + 1)][bb], qf[kk], s[bb]);
-      }
-    }
-
-    // ---- mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
     const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
     if (edge) {
 #pragma unroll
@@ -409,83 +386,192 @@ fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * bb + 16 * (i >> 3) + 8 * h + (i & 7);
           const bool dead = (key >= kv_len) || (CAUSAL && key > qi);
-          s[bb][i] = dead ? NEG_INF : s[bb][i];
+          sn[bb][i] = dead ? NEG_INF : sn[bb][i];
         }
     }
-
-    // ---- row max (in-lane over 32 keys, then across the two lane halves)
-    float mx = NEG_INF;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
+  };
+  // row max over the lane's 32 keys, then across the two lane halves, and the
+  // lazy rescale: the running max only moves (by a wave-uniform decision)
+  // when some row's max exceeds it by more than 2^TAU in probability
+  float msub = 0.f, alpha_next = 1.f;
+  auto finish_max = [&](float mx) {
     mx = fmaxf(mx, wave_half_swap(mx));
-    // lazy rescale, decided for the whole wave and kept branch-free so that
-    // the exponentials below stay in one basic block with the MFMAs
     const float m_new = fmaxf(m_run, mx * c);
     const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0;
     const float m_upd = moved ? m_new : m_run;
-    const float alpha = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
+    alpha_next = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
     m_run = m_upd;
-    const float msub = (m_run == NEG_INF) ? 0.f : m_run;
-
-    // ---- P = exp2(c*s - m) for chunk cc, with its row-sum share
-    float rs = 0.f;
-    auto softmax_chunk = [&](int cc) {
-      float pf[8];
+    msub = (m_run == NEG_INF) ? 0.f : m_run;
+  };
+  auto max16 = [&](const f32x16& x, float mx) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + e], c, -msub));
-        pout[cc][e] = (T)pf[e];
-      }
-      rs = Mma<T>::sum8(pout[cc], pf, rs);
-    };
-
-    // ---- O^T += V^T P^T of the previous tile, interleaved with this tile's exp
-    [&]<int... CC>(std::integer_sequence<int, CC...>) {
-      ([&] {
-        i16x4 vr[2 * DB];
-        read_v(vr, vprev, std::integral_constant<int, CC>{});
-        softmax_chunk(CC);
-        lds_wait(vr);
-        pv_chunk(vr, pin[CC]);
-      }(), ...);
-    }(std::make_integer_sequence<int, NC>{});
-    l_run = l_run * alpha + rs;
-    alpha_pend = alpha;
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);   // chains into v_max3
+    return mx;
   };
 
-  // Closing step of a wave: the last P V product only.
-  auto step_pv = [&](int t, vec8 (&pin)[NC]) {
-    top(t);
-    settle_alpha();
-    const uint32_t vprev = ((t + 1) & 1) * TILE;
-    [&]<int... CC>(std::integer_sequence<int, CC...>) {
-      ([&] {
-        i16x4 vr[2 * DB];
-        read_v(vr, vprev, std::integral_constant<int, CC>{});
-        lds_wait(vr);
-        pv_chunk(vr, pin[CC]);
-      }(), ...);
-    }(std::make_integer_sequence<int, NC>{});
+  // Operand reads for k-step kk: K of both 32-key blocks, and Q when it lives
+  // in LDS (same lane offsets: same row permutation and swizzle)
+  auto read_k = [&](const char* Ks, int kk, vec8 (&kr)[NB], vec8& qv) {
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) kr[bb] = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
+    if constexpr (QLDS) qv = *(const vec8*)(qwave + koff[kk]);
+    else qv = qf[kk];
+  };
+
+  // S_t = K_t Q^T with no VALU work to interleave (first tile only)
+  auto s_alone = [&](int t, f32x16 (&sn)[NB]) {
+    const char* Ks = smem + (t & 1) * TILE;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
+    vec8 kr[3][NB], qv[3];
+    read_k(Ks, 0, kr[0], qv[0]);
+    read_k(Ks, 1, kr[1], qv[1]);
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      if (kk + 2 < KT) read_k(Ks, kk + 2, kr[(kk + 2) % 3], qv[(kk + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) sn[bb] = Mma<T>::run(kr[kk % 3][bb], qv[kk % 3], sn[bb]);
+    }
+  };
+
+  // One tile: P_t V_t into O, S_{t+1} (when has_next) with its max.  The
+  // transposing V reads run one 16-key chunk ahead of their MFMAs (chunk 0 is
+  // issued near the end of stretch A, when the K prefetch registers free up).
+  auto tile = [&](int t, bool has_next, f32x16 (&sc)[NB], f32x16 (&sn)[NB]) {
+    // O and l pick up the rescale owed to tile t's max (a rare branch for O)
+    if (__builtin_amdgcn_ballot_w64(alpha_next != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha_next;
+    }
+    l_run *= alpha_next;
+    const float ms = msub;
+    float rs = 0.f;
+    vec8 pc[NC];
+    const uint32_t vst = (t & 1) * TILE;
+    i16x4 vr0[2 * DB], vr1[2 * DB], vr2[2 * DB], vr3[2 * DB];
+    auto mma_chunk = [&](i16x4 (&vr)[2 * DB], int db, const vec8& p) {
+      const i16x8 w = __builtin_shufflevector(vr[2 * db], vr[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = Mma<T>::run(__builtin_bit_cast(vec8, w), p, o[db]);
+    };
+
+    // ---- A: S_{t+1} with the exp2 of chunks 0-1 of S_t
+    if (has_next) {
+      const char* Ks = smem + ((t + 1) & 1) * TILE;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
+      // K (and Q) operands two k-steps ahead of their MFMAs
+      vec8 kr[3][NB], qv[3];
+      read_k(Ks, 0, kr[0], qv[0]);
+      read_k(Ks, 1, kr[1], qv[1]);
+#pragma unroll
+      for (int kk = 0; kk < KT; ++kk) {
+        if (kk + 2 < KT) read_k(Ks, kk + 2, kr[(kk + 2) % 3], qv[(kk + 2) % 3]);
+        if (kk == KT - 2) read_v(vr0, vst, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) sn[bb] = Mma<T>::run(kr[kk % 3][bb], qv[kk % 3], sn[bb]);
+        // 16 exponentials spread over the KT k-steps
+        constexpr int PER = 16 / KT;
+        exps(sc, ms, (kk * PER) / 8, (kk * PER) % 8, PER, rs);
+        if (((kk + 1) * PER) % 8 == 0) pack(sc, ((kk + 1) * PER) / 8 - 1, pc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      read_v(vr0, vst, std::integral_constant<int, 0>{});
+      exps(sc, ms, 0, 0, 8, rs);
+      exps(sc, ms, 1, 0, 8, rs);
+      pack(sc, 0, pc);
+      pack(sc, 1, pc);
+    }
+
+    // S_{t+1} is complete: mask it now (rare branch, outside the stretches)
+    if (has_next) mask(t + 1, sn);
+
+    // ---- B: chunks 0-1 of P V, exp2 of chunks 2-3
+    read_v(vr1, vst, std::integral_constant<int, 1>{});
+    exps(sc, ms, 2, 0, 4, rs);
+    lds_wait<2 * DB>(vr0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      mma_chunk(vr0, db, pc[0]);
+      exps(sc, ms, 2, 4 + db * (4 / DB), 4 / DB, rs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack(sc, 2, pc);
+    read_v(vr2, vst, std::integral_constant<int, 2>{});
+    exps(sc, ms, 3, 0, 4, rs);
+    lds_wait<2 * DB>(vr1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      mma_chunk(vr1, db, pc[1]);
+      exps(sc, ms, 3, 4 + db * (4 / DB), 4 / DB, rs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack(sc, 3, pc);
+    l_run += rs;
+
+    // ---- C: chunks 2-3 of P V, row max of S_{t+1}
+    float mx = NEG_INF;
+    read_v(vr3, vst, std::integral_constant<int, 3>{});
+    lds_wait<2 * DB>(vr2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) mma_chunk(vr2, db, pc[2]);
+    if (has_next) mx = max16(sn[0], mx);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_wait<0>(vr3);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) mma_chunk(vr3, db, pc[3]);
+    if (has_next) mx = max16(sn[NB - 1], mx);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) finish_max(mx);
   };
 
   // tiles this wave computes (a causal wave stops at its diagonal)
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
-  int t = 0;
-  for (; t + 1 < n_w; t += 2) {
-    step_full(t, pA, pB);
-    step_full(t + 1, pB, pA);
+
+  // Round r (r = 0 .. ntile): wait for the copies of round r-1, barrier, then
+  // start the copies of K_{r+1} and V_r into the buffers tile r-1 used.
+  auto top = [&](int r) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (r + 1 < ntile) issue(Kp, r + 1, smem + ((r + 1) & 1) * TILE, false);
+    if (r < ntile) issue(Vp, r, smem + 2 * TILE + (r & 1) * TILE, true);
+  };
+
+  issue(Kp, 0, smem, false);
+  top(0);
+  f32x16 sA[NB], sB[NB];
+  s_alone(0, sA);
+  mask(0, sA);
+  {
+    float mx = NEG_INF;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) mx = max16(sA[bb], mx);
+    finish_max(mx);
   }
-  if (t < n_w) {
-    step_full(t, pA, pB);
-    step_pv(t + 1, pB);
+  int t = 0;
+  for (; t + 2 < n_w; t += 2) {          // unrolled by two: the S sets swap roles
+    top(t + 1);
+    tile(t, true, sA, sB);
+    top(t + 2);
+    tile(t + 1, true, sB, sA);
+  }
+  if (t + 1 < n_w) {
+    top(t + 1);
+    tile(t, true, sA, sB);
+    top(t + 2);
+    tile(t + 1, false, sB, sA);
     t += 2;
   } else {
-    step_pv(t, pA);
+    top(t + 1);
+    tile(t, false, sA, sB);
     t += 1;
   }
-  for (; t <= ntile; ++t) top(t);
+  for (int r = t + 1; r <= ntile; ++r) top(r);
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + wave_half_swap(l_run);
@@ -509,26 +595,61 @@ fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, int BN>
-static hipError_t launch_t(const FwdParams& p, int causal, int varlen, hipStream_t s) {
-  dim3 grid(p.grid), block(kThreads);
-  if (varlen) {
-    if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, BN, false, true>), grid, block, 0, s, p);
-  } else {
-    if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, BN, false, false>), grid, block, 0, s, p);
-  }
+// Dynamic LDS bytes of a forward kernel instance: K and V double buffers, plus
+// the Q block for d = 128.
+template <int D, int BN, int NW>
+constexpr int fwd_lds_bytes() {
+  return 4 * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
+}
+
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN>
+static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
+  constexpr int lds = fwd_lds_bytes<D, BN, NW>();
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN>), dim3(p.grid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
-  if (dtype == 0) {
-    return d == 128 ? launch_t<__bf16, 128, 64>(p, causal, varlen, s)
-                    : launch_t<__bf16, 64, 64>(p, causal, varlen, s);
+template <typename T, int D, int BN, int NW>
+static hipError_t launch_t(const FwdParams& p, int causal, int varlen, hipStream_t s) {
+  if (varlen) {
+    return causal ? launch_one<T, D, BN, NW, true, true>(p, s) : launch_one<T, D, BN, NW, false, true>(p, s);
   }
-  return d == 128 ? launch_t<_Float16, 128, 64>(p, causal, varlen, s)
-                  : launch_t<_Float16, 64, 64>(p, causal, varlen, s);
+  return causal ? launch_one<T, D, BN, NW, true, false>(p, s) : launch_one<T, D, BN, NW, false, false>(p, s);
+}
+
+// Query rows per workgroup: 256 (8 waves, one workgroup per CU, each K/V tile
+// shared by 256 queries) for dense problems, 128 (4 waves, two workgroups per
+// CU) for ragged batches, where a smaller block wastes less on short
+// sequences.  ATTN_BLOCK_M=128|256 overrides the choice for tuning sweeps.
+int fwd_block_m(int dtype, int d, int varlen) {
+  (void)dtype;
+  (void)d;
+  static const int forced = [] {
+    const char* e = getenv("ATTN_BLOCK_M");
+    const int v = e ? atoi(e) : 0;
+    return (v == 128 || v == 256) ? v : 0;
+  }();
+  if (forced) return forced;
+  return varlen ? 128 : 256;
+}
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  const int bm = fwd_block_m(dtype, d, varlen);
+  if (bm == 256) {
+    if (dtype == 0)
+      return d == 128 ? launch_t<__bf16, 128, 64, 8>(p, causal, varlen, s)
+                      : launch_t<__bf16, 64, 64, 8>(p, causal, varlen, s);
+    return d == 128 ? launch_t<_Float16, 128, 64, 8>(p, causal, varlen, s)
+                    : launch_t<_Float16, 64, 64, 8>(p, causal, varlen, s);
+  }
+  if (dtype == 0)
+    return d == 128 ? launch_t<__bf16, 128, 64, 4>(p, causal, varlen, s)
+                    : launch_t<__bf16, 64, 64, 4>(p, causal, varlen, s);
+  return d == 128 ? launch_t<_Float16, 128, 64, 4>(p, causal, varlen, s)
+                  : launch_t<_Float16, 64, 64, 4>(p, causal, varlen, s);
 }
 
 }  // namespace attn

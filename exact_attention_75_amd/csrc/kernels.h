@@ -9,8 +9,7 @@
 
 namespace attn {
 
-constexpr int kBlockM = 128;  // query rows per workgroup (4 waves x 32)
-constexpr int kThreads = 256;
+constexpr int kBlockMMin = 128;  // smallest query block any kernel uses
 
 struct FwdParams {
   const void* q;
@@ -54,6 +53,11 @@ struct PrepassParams {
   int B, S, H, d;
   int transpose_out;
 };
+
+// Query rows per workgroup of the bf16/fp16 forward for this configuration.
+int fwd_block_m(int dtype, int d, int varlen);
+// Query rows per workgroup of the fp8 forward.
+int fwd_fp8_block_m();
 
 // Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
