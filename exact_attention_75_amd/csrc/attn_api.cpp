@@ -137,6 +137,7 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
   if (rc) return rc;
   if (d != 128) return ATTN_ERR_HEADDIM;
+  if (Sk % 16 != 0) return ATTN_ERR_SHAPE;   // 16-byte aligned rows of V^T
   attn::Fp8FwdParams p{};
   p.q8 = q8;
   p.k8 = k8;
@@ -196,6 +197,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E4M3_HADAMARD) {
     if (varlen) return ATTN_ERR_ARG;
     if (d != 128) return ATTN_ERR_HEADDIM;
+    if (Sk % 16 != 0) return ATTN_ERR_SHAPE;
     const long long nbq = (Sq + 127) / 128, nbk = (Sk + 127) / 128;
     const size_t qb = (size_t)B * Sq * Hq * d, kb = (size_t)B * Sk * Hkv * d;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };

@@ -1,7 +1,404 @@
-// attn_fp8.hip -- placeholder until the fp8 kernels land.
+// attn_fp8.hip -- fp8 (OCP E4M3) path of the attention forward for gfx950.
+//
+// Two kernels:
+//  * prepass_kernel: per (batch, head, block of 128 rows) -- optional signed
+//    128-point Hadamard rotation of each row in fp32, the block's amax, the
+//    fp32 scale s = amax / 448 (1 for an all-zero block), and the codes
+//    E4M3(clip(x / s, -448, 448)) with round-to-nearest-even.  This is the
+//    per-block scaling and incoherence processing of "FlashAttention-3 Deep
+//    Dive" (mojostudio.in), section 4; 448 is that section's clip bound and
+//    the format's largest finite value.  The codes are written row-major, or
+//    transposed (token index innermost) for V, whose second-GEMM operand
+//    wants the key index contiguous.
+//  * fwd_fp8_kernel: the fused forward with both GEMMs on the fp8 MFMA
+//    (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernel_common.h"
 #include "kernels.h"
+
 namespace attn {
+
 int fwd_fp8_block_m() { return 128; }
-hipError_t launch_fwd_fp8(const Fp8FwdParams&, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_prepass(const PrepassParams&, hipStream_t) { return hipErrorNotSupported; }
+
+// ============================================================================
+// prepass
+// ============================================================================
+//
+// One workgroup of 256 threads per block of 128 rows; thread t owns row t/2,
+// channels 64*(t%2) .. +63, in registers.  The rotation's last butterfly
+// stage (distance 64) pairs the two threads of a row, neighbouring lanes.
+
+__device__ __forceinline__ float lane_xor1(float x) {
+  // value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2])
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+__global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
+  constexpr int ROWS = 128, D = 128, HALF = 64;
+  const int nblk = (p.S + ROWS - 1) / ROWS;
+  const int blk = blockIdx.x % nblk;
+  const int h = (blockIdx.x / nblk) % p.H;
+  const int b = blockIdx.x / (nblk * p.H);
+  const int tid = threadIdx.x;
+  const int r = tid >> 1, half = tid & 1;
+  const int row0 = blk * ROWS;
+  const int nrows = min(ROWS, p.S - row0);
+  const bool live = r < nrows;
+
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tT[D][ROWS + 16];   // transposed codes
+
+  // ---- load the thread's 64 channels of its row
+  float x[HALF];
+  const long long rowidx = ((long long)b * p.S + row0 + r) * p.H + h;
+  const float* src = p.x + rowidx * D + half * HALF;
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const float4 v = *(const float4*)(src + i);
+      x[i] = v.x;
+      x[i + 1] = v.y;
+      x[i + 2] = v.z;
+      x[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) x[i] = 0.f;
+  }
+
+  // ---- optional rotation: x <- (x * signs) H_128 / sqrt(128), in fp32
+  if (p.signs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) x[i] *= p.signs[half * HALF + i];
+#pragma unroll
+    for (int len = 1; len < HALF; len <<= 1)
+#pragma unroll
+      for (int i = 0; i < HALF; ++i)
+        if ((i & len) == 0) {
+          const float a = x[i], c = x[i + len];
+          x[i] = a + c;
+          x[i + len] = a - c;
+        }
+    // distance-64 stage across the two threads of the row
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const float other = lane_xor1(x[i]);
+      x[i] = half == 0 ? x[i] + other : other - x[i];
+    }
+    const float norm = 0.08838834764831845f;   // 1 / sqrt(128)
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) x[i] *= norm;
+  }
+
+  // ---- block amax
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) am = fmaxf(am, fabsf(x[i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = am > 0.f ? am / 448.0f : 1.0f;
+  if (tid == 0) p.descale[((long long)b * p.H + h) * nblk + blk] = s;
+
+  // ---- quantise: E4M3(clip(x / s)), round to nearest even
+  uint32_t q[HALF / 4];
+#pragma unroll
+  for (int i = 0; i < HALF; i += 4) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[i + j] / s, -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+    q[i / 4] = (uint32_t)w;
+  }
+
+  if (!p.transpose_out) {
+    if (live) {
+      uint8_t* dst = p.x8 + rowidx * D + half * HALF;
+#pragma unroll
+      for (int i = 0; i < HALF / 16; ++i)
+        *(uint4*)(dst + 16 * i) = make_uint4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+    }
+    return;
+  }
+
+  // ---- transposed output [B, H, d, S] through LDS
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) tT[half * HALF + i][r] = (uint8_t)(q[i >> 2] >> (8 * (i & 3)));
+  __syncthreads();
+  const int c = tid >> 1;                 // channel written by this thread
+  const int s0 = (tid & 1) * HALF;        // its 64 tokens of the block
+  uint8_t* dst = p.x8 + (((long long)b * p.H + h) * D + c) * p.S + row0 + s0;
+  if (s0 + HALF <= nrows && ((p.S & 15) == 0)) {
+#pragma unroll
+    for (int i = 0; i < HALF / 16; ++i) *(uint4*)(dst + 16 * i) = *(const uint4*)(&tT[c][s0 + 16 * i]);
+  } else {
+    for (int i = 0; i < HALF && s0 + i < nrows; ++i) dst[i] = tT[c][s0 + i];
+  }
+}
+
+hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
+  const int nblk = (p.S + 127) / 128;
+  const long long grid = (long long)p.B * p.H * nblk;
+  hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// fp8 forward
+// ============================================================================
+//
+// A workgroup of 4 waves owns 128 query rows (one Q scale block), each wave
+// 32 rows; two workgroups share a CU.  Tiles of 64 keys (half a K/V scale
+// block).  Per tile and wave:
+//   S^T = K Q^T  : 2 blocks of 32 keys x 2 k-steps of 64 channels, on
+//                  v_mfma_scale_f32_32x32x64_f8f6f4 (E8M0 operand scales = 1)
+//   O^T += V^T P^T: one MFMA per 32 output channels, K = the tile's 64 keys.
+// Key rows of block b are fed in the order pi_b(r) = 32*bit2(r) + 16 b +
+// 4*(r >> 3) + (r & 3), which makes the 16 accumulator elements of lane half
+// h in block b the keys 32 h + 16 b + 0..15: the lane's 32 probabilities are
+// then the 32 consecutive keys the second MFMA's B operand wants, and V^T
+// (token index innermost, from the prepass) gives the A operand as plain
+// 32-byte LDS reads.
+//
+// Scales: scores are sq * sk_t * (Q~ K~^T) (sq per 128 query rows, sk_t per
+// 128 keys), folded into the exp2 argument.  Probabilities are produced as
+// P' = 2^8 exp2(c s - m) <= 256 with the exact running max (no lazy
+// threshold), so they use the upper part of the E4M3 range; the 2^8 cancels
+// in O / l.  O is accumulated in units of the current V block's scale and
+// rescaled when the block changes (every second tile).
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// K tile row r (128 bytes = 8 chunks): chunk c stored at c ^ swz_k8(r)
+__device__ __forceinline__ int swz_k8(int r) { return ((r >> 1) & 3) | ((r >> 3) & 4); }
+// V^T tile row r (64 bytes = 4 chunks): chunk c stored at c ^ swz_v8(r)
+__device__ __forceinline__ int swz_v8(int r) { return (r >> 2) & 3; }
+// key of MFMA row r in block b of a 64-key tile
+__device__ __forceinline__ int key_perm8(int r, int b) { return 32 * ((r >> 2) & 1) + 16 * b + 4 * (r >> 3) + (r & 3); }
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_fp8_kernel(Fp8FwdParams p) {
+  constexpr int NW = 4, BM = 128, BN = 64, D = 128;
+  constexpr int KROW = D;               // bytes per K row
+  constexpr int VROW = BN;              // bytes per V^T row (keys of a tile)
+  constexpr int TILE = BN * KROW;       // 8 KiB, same for V^T (D * VROW)
+  constexpr int LOADS = TILE / 16 / (NW * 64);   // DMA instructions per wave per tensor
+  constexpr float NEG_INF = -__builtin_inff();
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];   // [K0 | K1 | V0 | V1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, mblk;
+  tile_decode(p.tm, blockIdx.x, b, hq, mblk);
+  const int hkv = hq / p.group;
+  const int q_len = p.Sq, kv_len = p.Sk;
+  const int nbq = (p.Sq + 127) / 128, nbk = (p.Sk + 127) / 128;
+  const int qs = p.Hq * D, ks = p.Hkv * D;
+  const uint8_t* Qp = p.q8 + (long long)b * p.Sq * qs + hq * D;
+  const uint8_t* Kp = p.k8 + (long long)b * p.Sk * ks + hkv * D;
+  const uint8_t* Vt = p.v8t + ((long long)b * p.Hkv + hkv) * D * p.Sk;
+  const float* ksc = p.k_descale + ((long long)b * p.Hkv + hkv) * nbk;
+  const float* vsc = p.v_descale + ((long long)b * p.Hkv + hkv) * nbk;
+  const float sq = p.q_descale[((long long)b * p.Hq + hq) * nbq + mblk];
+
+  const int q0 = mblk * BM;
+  const int qw = q0 + wave * 32;
+  const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;
+  const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
+  const int ntile = (kv_end + BN - 1) / BN;
+  const int qi = qw + l32;
+
+  // Q fragment: lane holds query qi, channels 64 kk + 32 h .. +31
+  i32x8 qf[2];
+  {
+    const int qrow = qi < q_len ? qi : q_len - 1;
+    const uint8_t* qr = Qp + (long long)qrow * qs + 32 * h;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const i32x4 lo = *(const i32x4*)(qr + 64 * kk);
+      const i32x4 hi = *(const i32x4*)(qr + 64 * kk + 16);
+      qf[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+
+  // K / V^T copies (direct to LDS, swizzled through the fetch addresses)
+  uint32_t kdma[LOADS], vdma[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = (wave * LOADS + i) * 64 + lane;
+    const int kr = pos >> 3, kc = pos & 7;
+    kdma[i] = (uint32_t)(kr * ks + ((kc ^ swz_k8(kr)) << 4));
+    const int vr = pos >> 2, vc = pos & 3;
+    vdma[i] = (uint32_t)(vr * p.Sk + ((vc ^ swz_v8(vr)) << 4));
+  }
+  auto issue = [&](int t, int stage) {
+    const int j0 = t * BN;
+    copy_rows_to_lds<LOADS>((const void*)(Kp + (long long)j0 * ks), (uint32_t)(kv_len - j0) * (uint32_t)ks,
+                            smem + stage * TILE + wave * LOADS * 1024, kdma);
+    copy_rows_to_lds<LOADS>((const void*)(Vt + j0), (uint32_t)(D * p.Sk - j0),
+                            smem + (2 + stage) * TILE + wave * LOADS * 1024, vdma);
+  };
+
+  // per-lane LDS read offsets
+  int koff[2][2];   // [block][kk]: key row pi_b(l32), chunks 4 kk + 2 h (+1)
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r = key_perm8(l32, bb);
+      koff[bb][kk] = r * KROW + (((4 * kk + 2 * h) ^ swz_k8(r)) << 4);
+    }
+  int voff[4];      // [db]: V^T row 32 db + l32, chunks 2 h (+1)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int r = 32 * db + l32;
+    voff[db] = r * VROW + (((2 * h) ^ swz_v8(r)) << 4);
+  }
+  // the second chunk of each 32-byte read: the XOR keeps chunks 2h and 2h+1
+  // adjacent only up to the swizzle, so address it on its own
+  int koff2[2][2], voff2[4];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r = key_perm8(l32, bb);
+      koff2[bb][kk] = r * KROW + (((4 * kk + 2 * h + 1) ^ swz_k8(r)) << 4);
+    }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int r = 32 * db + l32;
+    voff2[db] = r * VROW + (((2 * h + 1) ^ swz_v8(r)) << 4);
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m_run = NEG_INF, l_run = 0.f;
+  float sv_cur = 0.f;     // V scale O is currently expressed in (0: none yet)
+  const float cbase = p.scale_log2 * sq;
+
+  const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
+
+  issue(0, 0);
+  for (int t = 0; t < ntile; ++t) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < ntile) issue(t + 1, (t + 1) & 1);
+    if (t >= n_w) continue;
+    const char* Ks = smem + (t & 1) * TILE;
+    const char* Vs = smem + (2 + (t & 1)) * TILE;
+    const int j0 = t * BN;
+    const float c = cbase * ksc[j0 >> 7];
+    const float sv = vsc[j0 >> 7];
+
+    // ---- S^T = K Q^T
+    f32x16 s[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      s[bb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x4 lo = *(const i32x4*)(Ks + koff[bb][kk]);
+        const i32x4 hi = *(const i32x4*)(Ks + koff2[bb][kk]);
+        s[bb] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf[kk], s[bb]);
+      }
+    }
+    // ---- mask: element i of block bb is key j0 + 32 h + 16 bb + i
+    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
+    if (edge) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * h + 16 * bb + i;
+          const bool dead = (key >= kv_len) || (CAUSAL && key > qi);
+          s[bb][i] = dead ? NEG_INF : s[bb][i];
+        }
+    }
+    // ---- exact running max
+    float mx = NEG_INF;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
+    mx = fmaxf(mx, wave_half_swap(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float msub = (m_run == NEG_INF) ? 0.f : m_run;
+    // O re-expressed in this tile's V scale, together with the max rescale
+    const float f = alpha * (sv_cur == 0.f ? 1.f : sv_cur / sv);
+    sv_cur = sv;
+    if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= f;
+    }
+    // ---- P' = 2^8 exp2(c s - m) -> E4M3; row sum over the fp32 values
+    float rs = 0.f;
+    i32x8 pk;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * w + j;           // 0..31: block k / 16, element k % 16
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k >> 4][k & 15], c, 8.0f - msub));
+        rs += e[j];
+      }
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
+    }
+    l_run = l_run * alpha + rs;
+    // ---- O^T += V^T P'^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i32x4 lo = *(const i32x4*)(Vs + voff[db]);
+      const i32x4 hi = *(const i32x4*)(Vs + voff2[db]);
+      o[db] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
+    }
+  }
+
+  // ---- epilogue: O = O_acc * sv / l (bf16), LSE = ln2 (m - 8 + log2 l)
+  const float l_tot = l_run + wave_half_swap(l_run);
+  if (qi < q_len) {
+    const float scl = l_tot > 0.f ? sv_cur / l_tot : 0.f;
+    __bf16* orow = (__bf16*)p.o + ((long long)b * p.Sq + qi) * qs + hq * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+        bf4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g + e] * scl);
+        *(bf4*)(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (p.lse != nullptr && h == 0) {
+      const float lse = l_tot > 0.f ? (m_run - 8.0f + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+      p.lse[((long long)b * p.Hq + hq) * p.Sq + qi] = lse;
+    }
+  }
+}
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s) {
+  if (causal) hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3(p.grid), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3(p.grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace attn

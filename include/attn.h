@@ -91,7 +91,8 @@ enum attn_status {
  * dtype: an attn_dtype.  For the fp8 types q, k, v are fp32 and o is bf16;
  *   the quantised copies live in a library-owned, lazily grown device
  *   workspace (released by attn_release); the Hadamard variant uses the
- *   library's default sign vector (attn_default_signs).  fp8 needs d == 128.
+ *   library's default sign vector (attn_default_signs).  fp8 needs d == 128
+ *   and Sk a multiple of 16, and no cu_seqlens.
  * lse may be NULL when the caller does not want it.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -129,7 +130,8 @@ int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, 
  *   q_descale [B, Hq, ceil(Sq/128)], k_descale and v_descale
  *       [B, Hkv, ceil(Sk/128)] fp32 block scales,
  *   o [B, Sq, Hq, d] bf16, lse [B, Hq, Sq] fp32 (may be NULL).
- * d must be 128; dense only (no cu_seqlens).
+ * d must be 128 and Sk a multiple of 16 (16-byte aligned rows of v8t);
+ * dense only (no cu_seqlens).
  */
 int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                  const float* q_descale, const float* k_descale, const float* v_descale,
