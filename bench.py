@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for the HBM byte counters)")
@@ -100,6 +101,49 @@ def make_step(ea, w, dev_inp):
         if rc != 0:
             raise RuntimeError(f"attn_fwd failed: {L.attn_strerror(rc).decode()}")
     return step
+
+
+def fp8_leg(ea, name, steps, warmup, hadamard=False):
+    """fp8 workload: time the whole step (prepass of Q, K, V + fp8 attention
+    kernel) and, separately, the attention kernel alone on pre-quantised
+    operands (the dominant kernel; the pages' FP8 figures are kernel-only)."""
+    import torch
+    import workloads as W
+    w = W.CONFIGS[name]
+    inp = W.make_inputs(w)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    dt = "fp8_hadamard" if hadamard else "fp8"
+    L = ea.library()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    code = ea.ATTN_FP8_E4M3_HADAMARD if hadamard else ea.ATTN_FP8_E4M3
+
+    def full():
+        rc = L.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq,
+                        w.Hkv, w.Sq, w.Sk, w.d, float(w.scale), int(w.causal), None, code, st)
+        if rc != 0:
+            raise RuntimeError(L.attn_strerror(rc).decode())
+    signs = torch.tensor(ea.default_signs(), device="cuda") if hadamard else None
+    q8, sq = ea.fp8_prepass(q, signs=signs)
+    k8, sk = ea.fp8_prepass(k, signs=signs)
+    v8t, sv = ea.fp8_prepass(v, transpose_out=True)
+
+    def kernel():
+        rc = L.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), sq.data_ptr(), sk.data_ptr(),
+                            sv.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d,
+                            float(w.scale), int(w.causal), st)
+        if rc != 0:
+            raise RuntimeError(L.attn_strerror(rc).decode())
+    ms_full = time_steps(full, steps, warmup) / steps
+    ms_k = time_steps(kernel, steps, warmup) / steps
+    fl = flops_of(w)
+    return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.Sq} d={w.d} e4m3"
+                        f"{' +hadamard' if hadamard else ''} {'causal' if w.causal else 'full'}",
+            "kernel_ms": round(ms_k, 5), "kernel_tflops": round(fl / (ms_k * 1e-3) / 1e12, 2),
+            "kernel_pct_of_fp8_peak": round(100 * fl / (ms_k * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2),
+            "step_ms_with_prepass": round(ms_full, 5),
+            "step_tflops_with_prepass": round(fl / (ms_full * 1e-3) / 1e12, 2)}
 
 
 def time_steps(step, steps, warmup):
@@ -213,6 +257,10 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n * 4
         del src, dst
+    if not a.no_fp8:
+        out["fp8"] = {"c3fp8": fp8_leg(ea, "c3fp8", a.steps, a.warmup),
+                      "c5": fp8_leg(ea, "c5", max(5, a.steps // 5), 3),
+                      "c5_hadamard": fp8_leg(ea, "c5", max(5, a.steps // 5), 3, hadamard=True)}
     if a.extra:
         for name in ("c1", "c2", "c4"):
             if name == a.workload:
