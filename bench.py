@@ -30,9 +30,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16, fp8) and % of MFMA peak, 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
-KERNEL_SOURCES = {"bf16": "exact_attention_75_amd/csrc/attn_fwd.hip",
-                  "fp16": "exact_attention_75_amd/csrc/attn_fwd.hip",
-                  "fp8": "exact_attention_75_amd/csrc/attn_fp8.hip"}
+_FWD_SOURCES = ("exact_attention_75_amd/csrc/attn_fwd.hip", "exact_attention_75_amd/csrc/kernel_common.h")
+KERNEL_SOURCES = {"bf16": _FWD_SOURCES, "fp16": _FWD_SOURCES,
+                  "fp8": ("exact_attention_75_amd/csrc/attn_fp8.hip", "exact_attention_75_amd/csrc/kernel_common.h")}
 
 
 def parse():
@@ -52,8 +52,11 @@ def parse():
 
 
 def kernel_hash(dtype: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(name: str, dtype: str, launches_per_step: int):
