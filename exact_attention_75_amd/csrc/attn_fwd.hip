@@ -107,6 +107,9 @@ fwd_kernel(FwdParams p) {
   constexpr int DB = D / 32;           // 32-column blocks of O^T
   constexpr int ROW = D * 2;           // bytes per K/V row in LDS
   constexpr int TILE = BN * ROW;       // bytes per K or V tile
+  // K/V buffers per tensor: three when one 8-wave workgroup has the CU's LDS
+  // to itself (copies run two tiles ahead), two otherwise
+  constexpr int STAGES = (NW == 8) ? 3 : 2;
   constexpr int LOADS = BN * CPR / (NW * 64);   // DMA instructions per wave per tile
   constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
   constexpr float NEG_INF = -__builtin_inff();
@@ -115,9 +118,9 @@ fwd_kernel(FwdParams p) {
   // With d = 128 the Q block lives in LDS (its 32 registers per lane are
   // needed by the pipeline); with d = 64 it stays in registers.
   constexpr bool QLDS = (D == 128);
-  // [K stage 0 | K stage 1 | V stage 0 | V stage 1 | Q block (QLDS)]
+  // [K stages | V stages | Q block (QLDS)]
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const qsm = smem + 4 * TILE;
+  char* const qsm = smem + 2 * STAGES * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,22 +231,23 @@ fwd_kernel(FwdParams p) {
 
   // per-lane LDS byte offsets, invariant over tiles
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
-  int koff[KT];
-  {
-    const int r = qlane;                  // block bb adds 32 rows: an immediate offset
-#pragma unroll
-    for (int kk = 0; kk < KT; ++kk) koff[kk] = r * ROW + (((2 * kk + h) ^ swz_k<D>(r)) << 4);
-  }
-  uint32_t voff[DB];
+  // K (and Q) rows: lane reads row qlane, 16-byte chunk 2 kk + h, stored at
+  // chunk (2 kk + h) ^ swz_k(row).  The k-step bits (bit 5 up of the byte
+  // offset) and the rest are disjoint fields, so offset(kk) = koff0 ^ (kk << 5);
+  // block bb adds 32 rows, an immediate.
+  const int koff0 = qlane * ROW + (((h) ^ swz_k<D>(qlane)) << 4);
+  auto koff = [&](int kk) { return koff0 ^ (kk << 5); };
+  // V rows for the transposing reads: likewise offset(db) = voff0 ^ (db << 6)
+  // (the 32-channel block index sits above the in-block bits of the offset);
+  // chunk cc adds 16 rows and the second read 4 rows, immediates.
+  uint32_t voff0;
   {
     const int G = lane >> 4, i16 = lane & 15;
-    const int r = 8 * h + (i16 >> 2);     // chunk cc adds 16 rows, the second read 4 rows
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int dd = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
-      voff[db] = lds0 + 2 * TILE + r * ROW + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
-    }
+    const int r = 8 * h + (i16 >> 2);
+    const int dd = 16 * (G & 1) + 4 * (i16 & 3);
+    voff0 = r * ROW + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
   }
+  auto voff = [&](int db) { return (voff0 ^ (uint32_t)(db << 6)) + lds0 + STAGES * TILE; };
 
   f32x16 o[DB];
 #pragma unroll
@@ -252,9 +256,12 @@ fwd_kernel(FwdParams p) {
     // both V stages start as zeros, so that the rows past the end of a ragged
     // tile hold zeros or earlier V data, never arbitrary bit patterns
     typedef int i32x4 __attribute__((ext_vector_type(4)));
-    i32x4* z = (i32x4*)(smem + 2 * TILE);
+    i32x4* z = (i32x4*)(smem + STAGES * TILE);
 #pragma unroll
-    for (int i = tid; i < 2 * TILE / 16; i += NTHREADS) z[i] = i32x4{};
+    for (int i = tid; i < STAGES * TILE / 16; i += NTHREADS) z[i] = i32x4{};
+    // every wave's zeros must land before any wave's first V copy (issued
+    // ahead of the first round's barrier with three stages)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   float m_run = NEG_INF;   // running max of scale*log2(e)*s for the lane's query (same in both halves)
   // This lane half's share of the running sum of P, taken over the fp32
@@ -269,8 +276,9 @@ fwd_kernel(FwdParams p) {
     constexpr int CC = decltype(cc_tag)::value;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      vr[2 * db] = lds_tr16<CC * 16 * ROW>(voff[db] + vstage);
-      vr[2 * db + 1] = lds_tr16<CC * 16 * ROW + 4 * ROW>(voff[db] + vstage);
+      const uint32_t a = voff(db) + vstage;
+      vr[2 * db] = lds_tr16<CC * 16 * ROW>(a);
+      vr[2 * db + 1] = lds_tr16<CC * 16 * ROW + 4 * ROW>(a);
     }
   };
 
@@ -335,15 +343,16 @@ fwd_kernel(FwdParams p) {
   // Operand reads for k-step kk: K of both 32-key blocks, and Q when it lives
   // in LDS (same lane offsets: same row permutation and swizzle)
   auto read_k = [&](const char* Ks, int kk, vec8 (&kr)[NB], vec8& qv) {
+    const int ko = koff(kk);
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) kr[bb] = *(const vec8*)(Ks + koff[kk] + bb * 32 * ROW);
-    if constexpr (QLDS) qv = *(const vec8*)(qwave + koff[kk]);
+    for (int bb = 0; bb < NB; ++bb) kr[bb] = *(const vec8*)(Ks + ko + bb * 32 * ROW);
+    if constexpr (QLDS) qv = *(const vec8*)(qwave + ko);
     else qv = qf[kk];
   };
 
   // S_t = K_t Q^T with no VALU work to interleave (first tile only)
   auto s_alone = [&](int t, f32x16 (&sn)[NB]) {
-    const char* Ks = smem + (t & 1) * TILE;
+    const char* Ks = smem + (t % STAGES) * TILE;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
     vec8 kr[3][NB], qv[3];
@@ -371,7 +380,7 @@ fwd_kernel(FwdParams p) {
     const float ms = msub;
     float rs = 0.f;
     vec8 pc[NC];
-    const uint32_t vst = (t & 1) * TILE;
+    const uint32_t vst = (t % STAGES) * TILE;
     i16x4 vr0[2 * DB], vr1[2 * DB], vr2[2 * DB], vr3[2 * DB];
     auto mma_chunk = [&](i16x4 (&vr)[2 * DB], int db, const vec8& p) {
       const i16x8 w = __builtin_shufflevector(vr[2 * db], vr[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -380,7 +389,7 @@ fwd_kernel(FwdParams p) {
 
     // ---- A: S_{t+1} with the exp2 of chunks 0-1 of S_t
     if (has_next) {
-      const char* Ks = smem + ((t + 1) & 1) * TILE;
+      const char* Ks = smem + ((t + 1) % STAGES) * TILE;
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
       // K (and Q) operands two k-steps ahead of their MFMAs
@@ -457,15 +466,36 @@ fwd_kernel(FwdParams p) {
   // tiles this wave computes (a causal wave stops at its diagonal)
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
 
-  // Round r (r = 0 .. ntile): wait for the copies of round r-1, barrier, then
-  // start the copies of K_{r+1} and V_r into the buffers tile r-1 used.
+  // Round r (r = 0 .. ntile) precedes tile r-1's work (and the first tile's
+  // S).  Two stages: wait for all copies, barrier, start K_{r+1} and V_r into
+  // the buffers tile r-1 used.  Three stages: wait only for the copies of
+  // round r-2 and older (vmcnt counts in order; round r-1's stay in flight),
+  // barrier, start K_{r+2} and V_{r+1} into the buffers tile r-2 used.
+  auto kbuf = [&](int t) { return smem + (t % STAGES) * TILE; };
+  auto vbuf = [&](int t) { return smem + (STAGES + t % STAGES) * TILE; };
   auto top = [&](int r) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (r + 1 < ntile) issue(Kp, r + 1, smem + ((r + 1) & 1) * TILE, false);
-    if (r < ntile) issue(Vp, r, smem + 2 * TILE + (r & 1) * TILE, true);
+    if constexpr (STAGES == 2) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (r + 1 < ntile) issue(Kp, r + 1, kbuf(r + 1), false);
+      if (r < ntile) issue(Vp, r, vbuf(r), true);
+    } else {
+      const int prev = r >= 1 ? (int)(r + 1 < ntile) + (int)(r < ntile) : 0;  // copies of round r-1
+      if (prev == 2)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+      else if (prev == 1)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (r + 2 < ntile) issue(Kp, r + 2, kbuf(r + 2), false);
+      if (r + 1 < ntile) issue(Vp, r + 1, vbuf(r + 1), true);
+    }
   };
 
-  issue(Kp, 0, smem, false);
+  issue(Kp, 0, kbuf(0), false);
+  if constexpr (STAGES == 3) {
+    if (1 < ntile) issue(Kp, 1, kbuf(1), false);
+    issue(Vp, 0, vbuf(0), true);
+  }
   top(0);
   f32x16 sA[NB], sB[NB];
   s_alone(0, sA);
@@ -522,7 +552,7 @@ fwd_kernel(FwdParams p) {
 // the Q block for d = 128.
 template <int D, int BN, int NW>
 constexpr int fwd_lds_bytes() {
-  return 4 * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
+  return 2 * (NW == 8 ? 3 : 2) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
 }
 
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN>
