@@ -10,6 +10,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -19,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip"]
 ARCH = "gfx950"
 
 
@@ -32,7 +33,7 @@ def hipcc() -> str:
 
 def common_flags():
     return [
-        "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
+        "-O3", "-std=c++2c", "-fPIC", f"--offload-arch={ARCH}",
         # packed fp32 VALU ops stay off: the compiler must not form v_pk_* f32 ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -61,10 +62,45 @@ def compile_one(src: str, save_temps: str | None) -> str:
     return obj
 
 
+# Sources whose kernels keep data in AGPRs named in inline assembly: the
+# compiler must not use any AGPR itself there (see csrc/wide_regs.h).
+PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip"]
+
+
+def check_pinned_agprs(src: str) -> None:
+    """Compile `src` to device assembly and fail unless, in every kernel, AGPRs
+    appear only inside inline-assembly regions and nothing spills."""
+    asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
+    cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"assembly listing failed: {src}\n{r.stderr}")
+    agpr = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
+    in_asm = False
+    kernel = None
+    for line in open(asm):
+        if line.startswith("_Z") and line.rstrip().endswith(":"):
+            kernel = line.split(":")[0]
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        code = t.split(";")[0]
+        if kernel and not in_asm and code and not code.startswith(".") and agpr.search(code):
+            raise RuntimeError(f"{src}: compiler-generated AGPR use in {kernel}: {code}")
+        m = re.match(r"\.(vgpr_spill_count|private_segment_fixed_size):\s+(\d+)", t)
+        if m and int(m.group(2)) != 0:
+            raise RuntimeError(f"{src}: {m.group(1)} = {m.group(2)} (register spills)")
+
+
 def build(jobs: int = 4, save_temps: str | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: compile_one(s, save_temps), SOURCES))
+        list(ex.map(check_pinned_agprs, PINNED_AGPR_SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -75,7 +111,7 @@ def build(jobs: int = 4, save_temps: str | None = None) -> str:
     return LIB
 
 
-EXPECTED_KERNELS = ("fwd_kernel",)
+EXPECTED_KERNELS = ("fwd_kernel", "fwd_wide_kernel", "fwd_fp8_kernel", "prepass_kernel")
 
 
 def check_kernels(path: str) -> None:

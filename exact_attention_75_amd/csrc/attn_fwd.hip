@@ -55,41 +55,6 @@
 
 namespace attn {
 
-template <typename T>
-struct Mma;
-
-template <>
-struct Mma<__bf16> {
-  typedef bf16x8 vec8;
-  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mma<_Float16> {
-  typedef f16x8 vec8;
-  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// Swizzle of 16-byte chunks inside one LDS row of the K tile: chunk c of row
-// r is stored at position c ^ swz_k(r).  16 consecutive rows (the lanes that
-// read one chunk column together) land on 16 different chunk positions.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return (D == 128) ? (r & 15) : (r & 7);
-}
-
-// Swizzle of the V tile.  A transposing read covers 4 consecutive rows x 64
-// bytes (chunks 4j..4j+3); the XOR moves each of those rows to a different
-// 64-byte quarter of the bank space.
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return (D == 128) ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
-}
-
 // NW waves per workgroup, each owning 32 query rows.  NW == 4: two
 // workgroups share a CU and their waves interleave freely.  NW == 8: one
 // workgroup per CU, two waves per SIMD (wave w and w + 4), run as two groups
@@ -589,8 +554,20 @@ int fwd_block_m(int dtype, int d, int varlen) {
   return varlen ? 128 : 256;
 }
 
+// Dense d = 128 problems with 256-row blocks run the one-wave-per-SIMD
+// kernel (attn_fwd_wide.hip); ATTN_KERNEL=narrow selects this file's 8-wave
+// kernel instead, for comparisons.
+static bool use_wide() {
+  static const bool wide = [] {
+    const char* e = getenv("ATTN_KERNEL");
+    return !(e && e[0] == 'n');
+  }();
+  return wide;
+}
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
   const int bm = fwd_block_m(dtype, d, varlen);
+  if (bm == 256 && d == 128 && !varlen && use_wide()) return launch_fwd_wide(p, dtype, causal, s);
   if (bm == 256) {
     if (dtype == 0)
       return d == 128 ? launch_t<__bf16, 128, 64, 8>(p, causal, varlen, s)

@@ -1,0 +1,557 @@
+// attn_fwd_wide.hip -- fused attention forward for gfx950, d = 128 dense,
+// bf16/fp16, one wave per SIMD.
+//
+// Same computation as attn_fwd.hip (O = softmax(scale * Q K^T + mask) V and
+// the natural-log LSE, "FlashAttention-3 Deep Dive", introduction formula;
+// Hopper tag page contents 4.2 and 4.6 for the streaming softmax state), with
+// a different split of the work over the CU:
+//
+//  * A workgroup is 4 waves and owns BM = 256 query rows; each wave owns 64
+//    of them (two 32-row blocks) and has a SIMD to itself.  Every K or V
+//    fragment a wave reads from LDS feeds two MFMAs (one per 32-row block),
+//    which halves the LDS read traffic per FLOP of the 32-rows-per-wave
+//    layout; at the MFMA peak that layout needs about as many LDS bytes per
+//    clock as the LDS delivers.  Q stays in registers for the whole loop.
+//  * With one wave per SIMD all overlap of matrix and vector work happens
+//    inside the wave.  Iteration t runs
+//        A: S_t = K_t Q^T (32 MFMA)        with exp2 of 3/4 of S_{t-1}
+//        B: O += P_{t-1} V_{t-1} (32 MFMA) with the mask and row max of S_t
+//                                          and exp2 of its first quarter
+//    so the softmax of a tile runs under the matrix products of the two
+//    stretches around it (the pages' overlap of the GEMMs with the softmax,
+//    "flash-attention-3", "Why a schedule", within one instruction stream).
+//  * K and V tiles stream global -> LDS through double buffers of
+//    direct-to-LDS copies.  Every round issues the same copies (a copy past
+//    the last tile has an empty buffer range and writes zeros into a free
+//    buffer), so the loop has no branches around them.
+//  * The running max moves lazily (only when a row's max grows by more than
+//    2^8 in probability), so P <= 256 and the O rescale is a rare branch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernel_common.h"
+#include "kernels.h"
+#include "wide_regs.h"
+
+namespace attn {
+
+using namespace wide;
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+template <typename T, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd_wide_kernel(FwdParams p) {
+  typedef typename Mma<T>::vec8 vec8;
+  constexpr int NW = 4;                // waves per workgroup
+  constexpr int QB = 2;                // 32-row query blocks per wave
+  constexpr int BM = 32 * QB * NW;     // 256 query rows per workgroup
+  constexpr int BN = 64;               // keys per tile
+  constexpr int D = 128;
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int KT = D / 16;           // k-steps of the first GEMM
+  constexpr int NB = BN / 32;          // 32-key blocks per tile
+  constexpr int NC = BN / 16;          // 16-key chunks per tile (second GEMM)
+  constexpr int DB = D / 32;           // 32-column blocks of O^T
+  constexpr int ROW = D * 2;           // bytes per K/V row in LDS
+  constexpr int TILE = BN * ROW;       // 16 KiB per K or V tile
+  constexpr int LOADS = BN * CPR / (NW * 64);   // copies per wave per tensor per tile
+#ifndef ATTN_WIDE_STAGES
+#define ATTN_WIDE_STAGES 4
+#endif
+  constexpr int STAGES = ATTN_WIDE_STAGES;   // K and V ring depth
+  constexpr float TAU = 8.0f;
+  constexpr float NEG_INF = -__builtin_inff();
+  static_assert(LOADS == 4 && QB == 2 && DB == 4 && NB == 2 && KT == 8, "tile shape");
+  // [K ring | V ring]
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, mblk;
+  tile_decode(p.tm, blockIdx.x, b, hq, mblk);
+  const int q_len = p.Sq, kv_len = p.Sk;
+  const int hkv = hq / p.group;
+  const T* Qp = (const T*)p.q + (long long)b * p.q_batch_stride + hq * D;
+  const T* Kp = (const T*)p.k + (long long)b * p.kv_batch_stride + hkv * D;
+  const T* Vp = (const T*)p.v + (long long)b * p.kv_batch_stride + hkv * D;
+  T* Op = (T*)p.o + (long long)b * p.q_batch_stride + hq * D;
+  const long long lse_off = ((long long)b * p.Hq + hq) * p.Sq;
+  const int qs = p.q_tok_stride;
+  const int ks = p.kv_tok_stride;
+
+  const int q0 = mblk * BM;
+  const int qw = q0 + 64 * wave;                         // first query row of this wave
+  const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;
+  const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
+  const int ntile = (kv_end + BN - 1) / BN;
+  // key tiles this wave computes: up to its diagonal when causal, none when
+  // all its rows are past the end of the sequence
+  int n_w = CAUSAL ? min(ntile, (qw + 63) / BN + 1) : ntile;
+  if (qw >= q_len) n_w = 0;
+
+  // ---------------------------------------------------------------- Q, O
+  // B operand of S^T = K Q^T: lane holds query qw + 32 qb + l32, head-dim
+  // 16 kk + 8 h .. +7 (rows past the end repeat the last row; never stored).
+  // The loads land before the first round's barrier (vmcnt(0)).
+  o_zero();
+  {
+    auto qrow = [&](int qb) {
+      const int r = qw + 32 * qb + l32;
+      return Qp + (long long)(r < q_len ? r : q_len - 1) * qs + 8 * h;
+    };
+    const T* q0p = qrow(0);
+    const T* q1p = qrow(1);
+    q_load<0, 0>(q0p + 0);   q_load<0, 1>(q0p + 16);  q_load<0, 2>(q0p + 32);  q_load<0, 3>(q0p + 48);
+    q_load<0, 4>(q0p + 64);  q_load<0, 5>(q0p + 80);  q_load<0, 6>(q0p + 96);  q_load<0, 7>(q0p + 112);
+    q_load<1, 0>(q1p + 0);   q_load<1, 1>(q1p + 16);  q_load<1, 2>(q1p + 32);  q_load<1, 3>(q1p + 48);
+    q_load<1, 4>(q1p + 64);  q_load<1, 5>(q1p + 80);  q_load<1, 6>(q1p + 96);  q_load<1, 7>(q1p + 112);
+  }
+
+  // ---------------------------------------------------------------- K/V copies
+  // Lane L of copy i fetches the global 16-byte chunk that belongs at LDS
+  // position (wave*LOADS + i)*64 + L of the tile under the row swizzle.  Tiles
+  // past the last one get an empty range: the copy writes zeros.
+  uint32_t kdma[LOADS], vdma[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = (wave * LOADS + i) * 64 + lane;
+    const int row = pos / CPR, phys = pos % CPR;
+    kdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_k<D>(row)) << 4));
+    vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+  }
+  // the copies of tile t of K or V into ring buffer buf: source, size and
+  // destination, all wave-uniform
+  struct Copy {
+    const void* src;
+    uint32_t bytes;
+    char* dst;
+  };
+  auto copy_of = [&](const T* base, int t, char* buf) {
+    const bool live = t < ntile;
+    const int j0 = live ? t * BN : 0;
+    return Copy{(const void*)(base + (long long)j0 * ks),
+                live ? (uint32_t)(kv_len - j0) * (uint32_t)ks * 2u : 0u, buf + wave * LOADS * 1024};
+  };
+  auto issue = [&](const T* src, int t, char* buf, const uint32_t(&off)[LOADS]) {
+    const Copy cp = copy_of(src, t, buf);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) copy_row_to_lds(cp.src, cp.bytes, cp.dst + i * 1024, off[i]);
+  };
+  // ring slot of tile t (t >= -1)
+  auto slot_of = [&](int t) { return (t + STAGES) % STAGES; };
+  auto kbuf = [&](int t) { return smem + slot_of(t) * TILE; };
+  auto vbuf = [&](int t) { return smem + (STAGES + slot_of(t)) * TILE; };
+
+  // ---------------------------------------------------------------- LDS reads
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+  // K: lane reads key row key_perm(l32) (+32 for the second block, an
+  // immediate), chunk 2 kk + h stored at chunk (2 kk + h) ^ swz_k(row); the
+  // ring slot is added per iteration
+  uint32_t kaddr[KT];
+  {
+    const int r = key_perm(l32);
+    const uint32_t koff0 = r * ROW + ((h ^ swz_k<D>(r)) << 4);
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) kaddr[kk] = lds0 + (koff0 ^ (uint32_t)(kk << 5));
+  }
+  // V (transposing reads): channel block db at (voff0 ^ (db << 6)); chunk
+  // (16 rows) and the second read (4 rows) are immediates, the ring slot is
+  // added per iteration
+  uint32_t vaddr[DB];
+  {
+    const int G = lane >> 4, i16 = lane & 15;
+    const int r = 8 * h + (i16 >> 2);
+    const int dd = 16 * (G & 1) + 4 * (i16 & 3);
+    const uint32_t voff0 = r * ROW + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vaddr[db] = lds0 + STAGES * TILE + (voff0 ^ (uint32_t)(db << 6));
+  }
+  // K fragments of k-step KK of the tile at byte offset kst into register
+  // ring slot KK % 3
+  auto read_k = [&](uint32_t kst, auto kk_tag) {
+    constexpr int KK = decltype(kk_tag)::value;
+    const uint32_t a = kaddr[KK] + kst;
+    k_read<KK % 3, 0, 0>(a);
+    k_read<KK % 3, 1, 32 * ROW>(a);
+  };
+  // V chunk CC of the tile at byte offset vst into fragment buffer CC & 1
+  auto read_v = [&](uint32_t vst, auto cc_tag) {
+    constexpr int CC = decltype(cc_tag)::value;
+    constexpr int OFF = CC * 16 * ROW;
+    v_read<CC & 1, 0, OFF, 4 * ROW>(vaddr[0] + vst);
+    v_read<CC & 1, 1, OFF, 4 * ROW>(vaddr[1] + vst);
+    v_read<CC & 1, 2, OFF, 4 * ROW>(vaddr[2] + vst);
+    v_read<CC & 1, 3, OFF, 4 * ROW>(vaddr[3] + vst);
+  };
+
+  // ---------------------------------------------------------------- softmax state
+  const float c = p.scale_log2;
+  // per query block: running max (scale*log2e units), this lane half's share
+  // of the running sum over the fp32 probabilities, the exponent offset of
+  // the current tile and the factor O still owes for the last max move
+  float m_run[QB], l_run[QB], msub[QB], alpha[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = NEG_INF;
+    l_run[qb] = 0.f;
+    msub[qb] = 0.f;
+    alpha[qb] = 1.f;
+  }
+
+  // mask: element i of s[qb][bb] is key j0 + 32 bb + 16 (i/8) + 8 h + i%8 for
+  // query qw + 32 qb + l32
+  auto mask = [&](int t, f32x16(&sn)[QB][NB]) {
+    const int j0 = t * BN;
+    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
+    if (edge) {
+      // (an opaque statement keeps this rare block a branch instead of
+      // selects executed on every tile)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw + 32 * qb + l32;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j0 + 32 * bb + 16 * (i >> 3) + 8 * h + (i & 7);
+            const bool dead = (key >= kv_len) || (CAUSAL && key > qi);
+            sn[qb][bb][i] = dead ? NEG_INF : sn[qb][bb][i];
+          }
+      }
+    }
+  };
+  // row max of block qb in four parts of 8 elements, then across the lane
+  // halves and the lazy, wave-uniform decision to move the running max; l
+  // first picks up the pending sums of the previous tile (rs_prev)
+  float mxp[QB];
+  auto max_part = [&](f32x16(&sn)[QB][NB], int qb, int part) {
+    if (part == 0) mxp[qb] = NEG_INF;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mxp[qb] = fmaxf(mxp[qb], sn[qb][part >> 1][8 * (part & 1) + k]);
+    keep(mxp[qb]);
+  };
+  auto finish_max = [&](int qb, float rs_prev) {
+    const float mx = fmaxf(mxp[qb], wave_half_swap(mxp[qb]));
+    const float m_new = fmaxf(m_run[qb], mx * c);
+    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run[qb] + TAU) != 0;
+    const float m_upd = moved ? m_new : m_run[qb];
+    const float a = (m_upd == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_upd);
+    alpha[qb] = a;
+    l_run[qb] = (l_run[qb] + rs_prev) * a;
+    m_run[qb] = m_upd;
+    msub[qb] = (m_upd == NEG_INF) ? 0.f : m_upd;
+    keep(msub[qb]);
+  };
+  // exp2(c s - m) of element e of chunk (qb, cc), added to the row sum and
+  // written into the P fragment (qb, cc) one step later (reading a
+  // transcendental result in the next instruction costs a wait state)
+  struct Pend {
+    float x;
+    int qb, cc, e;
+    bool valid;
+  };
+  auto commit = [&](Pend& pd, float(&rs)[QB], vec8(&pc)[QB][NC]) {
+    if (pd.valid) {
+      rs[pd.qb] += pd.x;
+      pc[pd.qb][pd.cc][pd.e] = (T)pd.x;
+      keep(rs[pd.qb]);
+      if (pd.e == 7) keep_vec(pc[pd.qb][pd.cc]);
+      pd.valid = false;
+    }
+  };
+  auto ex1 = [&](Pend& pd, f32x16(&sc)[QB][NB], int qb, int cc, int e, float(&rs)[QB], vec8(&pc)[QB][NC]) {
+    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][cc >> 1][8 * (cc & 1) + e], c, -msub[qb]));
+    keep(x);
+    commit(pd, rs, pc);
+    pd = Pend{x, qb, cc, e, true};
+  };
+
+  // Round r: wait for the copies of round r-STAGES+1 and older (every round
+  // issues the same 2 LOADS copies, so STAGES-2 rounds stay in flight) and
+  // barrier; the round's copies -- K_{r+STAGES-1} into the slot of K_{r-1},
+  // V_{r+STAGES-2} into the slot of V_{r-2} -- go out one per k-step of the
+  // iteration's first stretch.  Iteration r reads K_r and V_{r-1}.
+  auto top_wait = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS * (STAGES - 2)) : "memory");
+  };
+  auto round_copy = [&](const Copy& kc, const Copy& vc, int i) {
+    if (i < LOADS) copy_row_to_lds(kc.src, kc.bytes, kc.dst + i * 1024, kdma[i]);
+    else copy_row_to_lds(vc.src, vc.bytes, vc.dst + (i - LOADS) * 1024, vdma[i - LOADS]);
+  };
+  auto top = [&](int r) {
+    top_wait();
+    issue(Kp, r + STAGES - 1, kbuf(r + STAGES - 1), kdma);
+    issue(Vp, r + STAGES - 2, vbuf(r + STAGES - 2), vdma);
+  };
+
+  // One iteration.  HS: S_t is computed (t < n_w); HP: tile
+  // t-1 is finished and P_{t-1} V_{t-1} added (t >= 1).  s_cur / p_cur
+  // receive tile t, s_prev / p_prev hold tile t-1.
+  float rs_a[QB] = {0.f, 0.f};   // sums of P_{t-1} computed in A (added before l's rescale)
+  auto iter = [&](int t, auto hs_tag, auto hp_tag, f32x16(&s_cur)[QB][NB],
+                  f32x16(&s_prev)[QB][NB], vec8(&p_cur)[QB][NC], vec8(&p_prev)[QB][NC]) {
+    constexpr bool HS = decltype(hs_tag)::value;
+    constexpr bool HP = decltype(hp_tag)::value;
+    // with S_t to compute, the round's copies go one per k-step of A
+    Copy kc{}, vc{};
+    if constexpr (HS) {
+      top_wait();
+      kc = copy_of(Kp, t + STAGES - 1, kbuf(t + STAGES - 1));
+      vc = copy_of(Vp, t + STAGES - 2, vbuf(t + STAGES - 2));
+    } else {
+      top(t);
+    }
+    const uint32_t kst = (uint32_t)(slot_of(t) * TILE);       // K_t
+    const uint32_t vst = (uint32_t)(slot_of(t - 1) * TILE);   // V_{t-1}
+    // O owes the rescale decided with the max of tile t-1 (rare)
+    if constexpr (HP) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0, 0)) {
+        acc_scale<0, 0>(alpha[0]);
+        acc_scale<0, 1>(alpha[0]);
+        acc_scale<0, 2>(alpha[0]);
+        acc_scale<0, 3>(alpha[0]);
+        acc_scale<1, 0>(alpha[1]);
+        acc_scale<1, 1>(alpha[1]);
+        acc_scale<1, 2>(alpha[1]);
+        acc_scale<1, 3>(alpha[1]);
+      }
+      alpha[0] = alpha[1] = 1.f;
+    }
+    rs_a[0] = rs_a[1] = 0.f;
+    float rs_b[QB] = {0.f, 0.f};
+
+    // exponentials of S_{t-1} done in A: 48 elements, chunks 1-3 of both
+    // query blocks in the order (0,1) (1,1) (0,2) (1,2) (0,3) (1,3)
+    Pend pa{0.f, 0, 0, 0, false}, pb{0.f, 0, 0, 0, false};
+    auto ex_a = [&](int i) {
+      const int g = i >> 3;
+      ex1(pa, s_prev, g & 1, 1 + (g >> 1), i & 7, rs_a, p_prev);
+    };
+
+    // ---- A: S_t = K_t Q^T, 6 exponentials of S_{t-1} per k-step
+    if constexpr (HS) {
+      read_k(kst, ic<0>{});
+      read_k(kst, ic<1>{});
+      auto kstep = [&](auto kk_tag) {
+        constexpr int KK = decltype(kk_tag)::value;
+        constexpr int R = KK % 3;
+        constexpr bool F = KK == 0;
+        round_copy(kc, vc, KK);
+        if constexpr (KK + 2 < KT) read_k(kst, ic<KK + 2>{});
+        if constexpr (HP && KK == KT - 2) read_v(vst, ic<0>{});
+        // LDS reads issued after k-step KK: up to two k-steps, and V chunk 0
+        constexpr int LEFT = 2 * ((KK + 2 < KT ? KK + 2 : KT - 1) - KK) + ((HP && KK >= KT - 2) ? 2 * DB : 0);
+        lgkm_wait<LEFT>();
+        // MFMA (bb, qb) with 2, 1, 2, 1 exponentials after it (the
+        // scheduling barriers keep each group behind its MFMA)
+        mfma_s<T, F, R, 0, 0, KK>(s_cur[0][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HP) { ex_a(6 * KK + 0); ex_a(6 * KK + 1); }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_s<T, F, R, 0, 1, KK>(s_cur[1][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HP) ex_a(6 * KK + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_s<T, F, R, 1, 0, KK>(s_cur[0][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HP) { ex_a(6 * KK + 3); ex_a(6 * KK + 4); }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_s<T, F, R, 1, 1, KK>(s_cur[1][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HP) ex_a(6 * KK + 5);
+        if constexpr (HP && KK == KT - 1) commit(pa, rs_a, p_prev);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      kstep(ic<0>{});
+      kstep(ic<1>{});
+      kstep(ic<2>{});
+      kstep(ic<3>{});
+      kstep(ic<4>{});
+      kstep(ic<5>{});
+      kstep(ic<6>{});
+      kstep(ic<7>{});
+    } else if constexpr (HP) {
+      read_v(vst, ic<0>{});
+#pragma unroll
+      for (int i = 0; i < 48; ++i) ex_a(i);
+      commit(pa, rs_a, p_prev);
+    }
+
+    // ---- B: P_{t-1} V_{t-1}; mask, row max and exp2 of chunk 0 of S_t
+    // vector work of slot j of chunk CC (after the chunk's j-th MFMA)
+    auto slot = [&](auto cc_tag, auto j_tag) {
+      constexpr int CC = decltype(cc_tag)::value;
+      constexpr int J = decltype(j_tag)::value;
+      if constexpr (HS) {
+        if constexpr (CC == 1) {
+          if constexpr (J == 0) { max_part(s_cur, 0, 0); max_part(s_cur, 0, 1); }
+          if constexpr (J == 1) { max_part(s_cur, 0, 2); max_part(s_cur, 0, 3); }
+          if constexpr (J == 2) finish_max(0, rs_a[0]);
+          if constexpr (J == 3) { max_part(s_cur, 1, 0); max_part(s_cur, 1, 1); }
+          if constexpr (J == 4) { max_part(s_cur, 1, 2); max_part(s_cur, 1, 3); }
+          if constexpr (J == 5) finish_max(1, rs_a[1]);
+        }
+        if constexpr (CC == 2) ex1(pb, s_cur, 0, 0, J, rs_b, p_cur);
+        if constexpr (CC == 3) ex1(pb, s_cur, 1, 0, J, rs_b, p_cur);
+        if constexpr (CC == 3 && J == 7) commit(pb, rs_b, p_cur);
+      }
+    };
+    if constexpr (HP) {
+      auto chunk = [&](auto cc_tag) {
+        constexpr int CC = decltype(cc_tag)::value;
+        constexpr int C = CC & 1;
+        if constexpr (CC + 1 < NC) {
+          read_v(vst, ic<CC + 1>{});
+          lgkm_wait<2 * DB>();
+        } else {
+          lgkm_wait<0>();
+        }
+        auto after = [&](auto j_tag) {
+          __builtin_amdgcn_sched_barrier(0);
+          slot(cc_tag, j_tag);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        mfma_o<T, 0, 0, C>(p_prev[0][CC]);
+        after(ic<0>{});
+        mfma_o<T, 1, 0, C>(p_prev[1][CC]);
+        after(ic<1>{});
+        mfma_o<T, 0, 1, C>(p_prev[0][CC]);
+        after(ic<2>{});
+        mfma_o<T, 1, 1, C>(p_prev[1][CC]);
+        after(ic<3>{});
+        mfma_o<T, 0, 2, C>(p_prev[0][CC]);
+        after(ic<4>{});
+        mfma_o<T, 1, 2, C>(p_prev[1][CC]);
+        after(ic<5>{});
+        mfma_o<T, 0, 3, C>(p_prev[0][CC]);
+        after(ic<6>{});
+        mfma_o<T, 1, 3, C>(p_prev[1][CC]);
+        after(ic<7>{});
+        // S_t may be read after these eight MFMA issues; mask it (rare)
+        if constexpr (HS && CC == 0) {
+          tie_s(s_cur);
+          mask(t, s_cur);
+        }
+      };
+      chunk(ic<0>{});
+      chunk(ic<1>{});
+      chunk(ic<2>{});
+      chunk(ic<3>{});
+    } else if constexpr (HS) {
+      pad_s(s_cur);
+      mask(t, s_cur);
+      slot(ic<1>{}, ic<0>{});
+      slot(ic<1>{}, ic<1>{});
+      slot(ic<1>{}, ic<2>{});
+      slot(ic<1>{}, ic<3>{});
+      slot(ic<1>{}, ic<4>{});
+      slot(ic<1>{}, ic<5>{});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ex1(pb, s_cur, 0, 0, e, rs_b, p_cur);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ex1(pb, s_cur, 1, 0, e, rs_b, p_cur);
+      commit(pb, rs_b, p_cur);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs_b[qb] + (HS ? 0.f : rs_a[qb]);
+  };
+
+  // ---------------------------------------------------------------- key loop
+  // Iterations 0 .. n_w: S_t (t < n_w) and P_{t-1} V_{t-1} (t >= 1).  Even
+  // iterations keep tile t in s0 / p0, odd ones in s1 / p1.
+  // prologue rounds -STAGES+1 .. -1: K_0 .. K_{STAGES-2} and V_{-1} (an
+  // empty copy, so that every round issues the same number of copies) ..
+  // V_{STAGES-3}
+#pragma unroll
+  for (int r = -STAGES + 1; r < 0; ++r) {
+    issue(Kp, r + STAGES - 1, kbuf(r + STAGES - 1), kdma);
+    issue(Vp, r + STAGES - 2 >= 0 ? r + STAGES - 2 : ntile, vbuf(r + STAGES - 2), vdma);
+  }
+  f32x16 s0[QB][NB], s1[QB][NB];
+  vec8 p0[QB][NC], p1[QB][NC];
+  typedef std::true_type Y;
+  typedef std::false_type N;
+  int t = 0;
+  if (n_w > 0) {
+    iter(0, Y{}, N{}, s0, s1, p0, p1);
+    t = 1;
+    for (; t + 2 <= n_w; t += 2) {
+      iter(t, Y{}, Y{}, s1, s0, p1, p0);
+      iter(t + 1, Y{}, Y{}, s0, s1, p0, p1);
+    }
+    // t is odd, t >= n_w - 1
+    if (t < n_w) {
+      iter(t, Y{}, Y{}, s1, s0, p1, p0);
+      iter(t + 1, N{}, Y{}, s0, s1, p0, p1);
+      t += 2;
+    } else {
+      iter(t, N{}, Y{}, s1, s0, p1, p0);
+      t += 1;
+    }
+  }
+  // idle rounds keep the barrier count equal across the waves
+  for (; t <= ntile; ++t) top(t);
+  // no copy may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  acc_read_pad();
+
+  // ---------------------------------------------------------------- epilogue
+  auto store = [&](auto qb_tag, const f32x16 (&ob)[DB]) {
+    constexpr int QBI = decltype(qb_tag)::value;
+    const float l_tot = l_run[QBI] + wave_half_swap(l_run[QBI]);
+    const int qi = qw + 32 * QBI + l32;
+    if (qi < q_len) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      T* orow = Op + (long long)qi * qs;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef T T4 __attribute__((ext_vector_type(4)));
+          T4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (T)(ob[db][4 * g + e] * inv);
+          *(T4*)(orow + 32 * db + 8 * g + 4 * h) = w;
+        }
+      if (p.lse != nullptr && h == 0) {
+        const float lse = l_tot > 0.f ? (m_run[QBI] + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+        p.lse[lse_off + qi] = lse;
+      }
+    }
+  };
+  {
+    const f32x16 ob[DB] = {acc_read<0, 0>(), acc_read<0, 1>(), acc_read<0, 2>(), acc_read<0, 3>()};
+    store(ic<0>{}, ob);
+  }
+  {
+    const f32x16 ob[DB] = {acc_read<1, 0>(), acc_read<1, 1>(), acc_read<1, 2>(), acc_read<1, 3>()};
+    store(ic<1>{}, ob);
+  }
+}
+
+template <typename T, bool CAUSAL>
+static hipError_t launch_wide_one(const FwdParams& p, hipStream_t s) {
+  constexpr int lds = 2 * ATTN_WIDE_STAGES * 64 * 128 * 2;   // K and V rings of 16 KiB tiles
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_wide_kernel<T, CAUSAL>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((fwd_wide_kernel<T, CAUSAL>), dim3(p.grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s) {
+  if (dtype == 0) return causal ? launch_wide_one<__bf16, true>(p, s) : launch_wide_one<__bf16, false>(p, s);
+  return causal ? launch_wide_one<_Float16, true>(p, s) : launch_wide_one<_Float16, false>(p, s);
+}
+
+}  // namespace attn

@@ -40,11 +40,32 @@ __device__ __forceinline__ void copy_rows_to_lds(const void* base, uint32_t byte
                                                  const uint32_t (&off)[N]) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // (the buffer-resource type exists only in the device pass of the compiler)
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+  // base and size are uniform; saying so keeps the resource in SGPRs even
+  // when they were computed with vector instructions
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  void* const ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 #pragma unroll
   for (int i = 0; i < N; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + i * 1024), 16, off[i], 0, 0, 0);
+#endif
+}
+
+// One direct-to-LDS copy of 16 bytes per lane: LDS bytes [dst, dst + 1024),
+// lane L the 16 bytes at offset 16 L, fetched from base + off (zeros at or
+// past `bytes`).
+__device__ __forceinline__ void copy_row_to_lds(const void* base, uint32_t bytes, char* dst, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  void* const ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, off, 0, 0, 0);
 #endif
 }
 
@@ -84,5 +105,56 @@ __device__ __forceinline__ void lds_wait(i16x4 (&r)[N]) {
   }
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read issued as inline assembly (ds_read_b128), for the same
+// reason as lds_tr16; wait for it with lds_wait().
+template <int OFF>
+__device__ __forceinline__ i32x4 lds_rd128(uint32_t addr) {
+  i32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
+template <int LEFT>
+__device__ __forceinline__ void lds_wait(i32x4 (&r)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(LEFT));
+}
+
+// MFMA 32x32x16 with fp32 accumulation for the two 16-bit input types.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Swizzle of 16-byte chunks inside one LDS row of the K tile: chunk c of row
+// r is stored at position c ^ swz_k(r).  16 consecutive rows (the lanes that
+// read one chunk column together) land on 16 different chunk positions.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return (D == 128) ? (r & 15) : (r & 7);
+}
+
+// Swizzle of the V tile.  A transposing read covers 4 consecutive rows x 64
+// bytes (chunks 4j..4j+3); the XOR moves each of those rows to a different
+// 64-byte quarter of the bank space.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return (D == 128) ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
 
 }  // namespace attn

@@ -61,6 +61,8 @@ int fwd_fp8_block_m();
 
 // Returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
+// d = 128 dense bf16/fp16 with 256-row blocks, one wave per SIMD.
+hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);
 
