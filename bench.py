@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16, fp8) and % of MFMA peak, 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
-_FWD_SOURCES = ("exact_attention_75_amd/csrc/attn_fwd.hip", "exact_attention_75_amd/csrc/kernel_common.h")
+_FWD_SOURCES = ("exact_attention_75_amd/csrc/attn_fwd.hip", "exact_attention_75_amd/csrc/attn_fwd_wide.hip",
+                "exact_attention_75_amd/csrc/wide_regs.h", "exact_attention_75_amd/csrc/kernel_common.h")
 KERNEL_SOURCES = {"bf16": _FWD_SOURCES, "fp16": _FWD_SOURCES,
                   "fp8": ("exact_attention_75_amd/csrc/attn_fp8.hip", "exact_attention_75_amd/csrc/kernel_common.h")}
 
