@@ -8,7 +8,9 @@ tables and no constants with the GPU path.
 
 Modules
   attention  the definition softmax(scale * Q K^T + mask) V with a per-row
-             natural-log LSE, the full score matrix materialised per head
+             natural-log LSE, the full score matrix materialised per head;
+             the same over a sub-range of the keys (the partial state of one
+             key split) and the combine formula that merges such partials
   fp8        OCP E4M3 encode/decode, per-128-row block quantisation, the
              Sylvester Hadamard matrix and the signed rotation
 

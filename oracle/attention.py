@@ -44,13 +44,14 @@ def _as_f64(x) -> np.ndarray:
 
 
 def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-               rows: Optional[np.ndarray] = None):
+               rows: Optional[np.ndarray] = None, key_offset: int = 0):
     """Softmax probabilities for one head.
 
     q [Sq, d], k [Sk, d] (fp64).  Returns (P [R, Sk], m [R], l [R]) for the
     selected query rows (all rows if ``rows`` is None), where
     P = exp(S - m) / l, S = scale * q k^T with -inf on masked entries,
-    m = row max of S, l = sum_j exp(S_ij - m_i).
+    m = row max of S, l = sum_j exp(S_ij - m_i).  ``key_offset`` is the
+    position of k's first row in the key sequence (for the causal mask).
     """
     Sq, Sk = q.shape[0], k.shape[0]
     if rows is None:
@@ -58,7 +59,7 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
     rows = np.asarray(rows, dtype=np.int64)
     s = scale * (q[rows] @ k.T)                      # [R, Sk]
     if causal:
-        j = np.arange(Sk)[None, :]
+        j = key_offset + np.arange(Sk)[None, :]
         s = np.where(j > rows[:, None], -np.inf, s)
     m = s.max(axis=1) if Sk > 0 else np.full(len(rows), -np.inf)
     m_safe = np.where(np.isfinite(m), m, 0.0)
@@ -70,7 +71,7 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
 
 
 def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
-                   rows: Optional[np.ndarray] = None, row_chunk: int = 1024):
+                   rows: Optional[np.ndarray] = None, row_chunk: int = 1024, key_offset: int = 0):
     """Attention for one head: q [Sq, d], k/v [Sk, d] -> (O [R, d], LSE [R])."""
     Sq = q.shape[0]
     if rows is None:
@@ -80,7 +81,7 @@ def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, ca
     L = np.full(len(rows), -np.inf, dtype=np.float64)
     for c0 in range(0, len(rows), row_chunk):
         r = rows[c0:c0 + row_chunk]
-        p, m, l = head_probs(q, k, scale, causal, r)
+        p, m, l = head_probs(q, k, scale, causal, r, key_offset)
         O[c0:c0 + len(r)] = p @ v
         with np.errstate(divide="ignore"):
             L[c0:c0 + len(r)] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
@@ -134,6 +135,62 @@ def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None,
             O[b, rsel, h] = o
             L[b, h, rsel] = l
     return O, L
+
+
+def partial_attention(q, k, v, scale: float, causal: bool, key_lo: int, key_hi: int):
+    """Attention of every query over the keys [key_lo, key_hi) only: the
+    partial state one split of the key axis produces in flash-decoding
+    (Hopper tag page, contents 10 "Split-KV and the Combine Kernel", 10.2
+    parallelisation over the KV sequence; the section bodies are absent from
+    the pages, so this is the plain reading).  Dense layout as ``attention``;
+    causal positions are absolute (key j hidden from query i when j > i).
+    Returns (O_p [B, Sq, Hq, d], LSE_p [B, Hq, Sq]); a row that sees no key of
+    the range gets O_p = 0 and LSE_p = -inf.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    lo, hi = max(0, key_lo), min(k.shape[1], key_hi)
+    O = np.zeros((B, Sq, Hq, v.shape[3]))
+    L = np.full((B, Hq, Sq), -np.inf)
+    if hi <= lo:
+        return O, L
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            o, l = head_attention(q[b, :, h], k[b, lo:hi, hk], v[b, lo:hi, hk], scale, causal,
+                                  key_offset=lo)
+            O[b, :, h] = o
+            L[b, h] = l
+    return O, L
+
+
+def combine(o_parts, lse_parts):
+    """Merge attention results over disjoint key sets into the result over
+    their union (the block-combine of two softmax states, Hopper tag page
+    contents 3.2.1, used for the split-KV combine, contents 10.2.1):
+
+        LSE = log sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) * O_p
+
+    o_parts [P, B, Sq, Hq, d], lse_parts [P, B, Hq, Sq] (natural-log LSE, O_p
+    normalised).  A part with LSE_p = -inf contributes nothing; a row whose
+    parts are all -inf gets O = 0, LSE = -inf.
+    """
+    o_parts = _as_f64(o_parts)
+    lse_parts = _as_f64(lse_parts)
+    m = lse_parts.max(axis=0)                                   # [B, Hq, Sq]
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe[None])                        # [P, B, Hq, Sq]; 0 for -inf parts
+    wsum = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(wsum > 0, m_safe + np.log(np.where(wsum > 0, wsum, 1.0)), -np.inf)
+    wn = np.where(wsum[None] > 0, w / np.where(wsum > 0, wsum, 1.0)[None], 0.0)
+    wo = np.transpose(wn, (0, 1, 3, 2))[..., None]              # [P, B, Sq, Hq, 1]
+    o_safe = np.where(wo > 0, o_parts, 0.0)
+    return (wo * o_safe).sum(axis=0), lse
 
 
 def attention_flops(Sq: int, Sk: int, d: int, causal: bool, B: int = 1, H: int = 1,
