@@ -9,6 +9,7 @@ or a call fails, an exception is raised.
 
     o, lse = fwd(q, k, v, causal=True)            # bf16 / fp16, dense or varlen
     o, lse = fwd(q32, k32, v32, dtype="fp8")      # fp32 inputs, fp8 GEMMs, bf16 out
+    o, lse = fwd_splitkv(q, k, v, num_splits=0)   # key axis split over workgroups
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "fp8_prepass", "library", "default_signs", "tile_of",
+__all__ = ["fwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
+           "default_signs", "tile_of",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
 ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3, ATTN_FP8_E4M3_HADAMARD = 0, 1, 2, 3
@@ -58,6 +60,12 @@ def library() -> ctypes.CDLL:
     L.attn_tile_of.restype = I
     L.attn_grid_size.argtypes = [I, I, I, I, I, IP, IP]
     L.attn_grid_size.restype = I
+    L.attn_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    L.attn_fwd_splitkv.restype = I
+    L.attn_split_plan.argtypes = [I, I, I, I, I, IP, IP]
+    L.attn_split_plan.restype = I
+    L.attn_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+    L.attn_combine.restype = I
     L.attn_strerror.argtypes = [I]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_release.argtypes = []
@@ -133,6 +141,64 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     rc = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                             float(scale), int(bool(causal)), _ptr(cu_seqlens), dt, _stream())
     _check(rc, "attn_fwd")
+    return o, lse
+
+
+def _kernel_dtype(*ts) -> int:
+    if all(t.dtype == torch.bfloat16 for t in ts):
+        return ATTN_BF16
+    if all(t.dtype == torch.float16 for t in ts):
+        return ATTN_FP16
+    raise ValueError("tensors must all be bf16 or all fp16")
+
+
+def split_plan(B: int, Hq: int, Sq: int, Sk: int, num_splits: int = 0) -> Tuple[int, int]:
+    """(number of key ranges, keys per range) that ``attn_fwd_splitkv`` uses."""
+    n, keys = ctypes.c_int(), ctypes.c_int()
+    _check(library().attn_split_plan(B, Hq, Sq, Sk, num_splits, ctypes.byref(n), ctypes.byref(keys)),
+           "attn_split_plan")
+    return n.value, keys.value
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                scale: Optional[float] = None, num_splits: int = 0,
+                return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense bf16/fp16 forward with the key axis split (``attn_fwd_splitkv``).
+
+    q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> o [B, Sq, Hq, d], lse [B, Hq, Sq].
+    num_splits 0 lets the library choose (``split_plan``)."""
+    _need_gpu(q, k, v)
+    dt = _kernel_dtype(q, k, v)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = library().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                                    float(scale), int(bool(causal)), int(num_splits), dt, _stream())
+    _check(rc, "attn_fwd_splitkv")
+    return o, lse
+
+
+def combine(o_part: torch.Tensor, lse_part: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
+            return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Merge split-KV partials (``attn_combine``).
+
+    o_part fp32 [P, B, Sq, Hq, d], lse_part fp32 [P, B, Hq, Sq] -> o [B, Sq, Hq, d]
+    in ``dtype`` (bf16 or fp16), lse [B, Hq, Sq]."""
+    _need_gpu(o_part, lse_part)
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    P, B, Sq, Hq, d = o_part.shape
+    if tuple(lse_part.shape) != (P, B, Hq, Sq):
+        raise ValueError("lse_part must be [P, B, Hq, Sq]")
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}[dtype]
+    o = torch.empty((B, Sq, Hq, d), dtype=dtype, device=o_part.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o_part.device) if return_lse else None
+    rc = library().attn_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), P, B, Hq, Sq, d, dt,
+                                _stream())
+    _check(rc, "attn_combine")
     return o, lse
 
 

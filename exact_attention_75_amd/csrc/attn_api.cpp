@@ -36,22 +36,25 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
   return ATTN_OK;
 }
 
-// --- fp8 workspace: one lazily grown device buffer per device -------------
+// --- workspaces: lazily grown device buffers, one per (use, device) -------
+// kWsFp8 holds the quantised operands of attn_fwd's fp8 types, kWsSplit the
+// split-KV partials; separate buffers, so the two paths never share memory.
 constexpr int kMaxDevices = 64;
+enum { kWsFp8 = 0, kWsSplit = 1, kWsKinds = 2 };
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-Workspace g_ws[kMaxDevices];
+Workspace g_ws[kWsKinds][kMaxDevices];
 std::mutex g_ws_mu;
 
-int workspace(size_t bytes, void** out) {
+int workspace(int kind, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_ARG;
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& w = g_ws[dev];
+  Workspace& w = g_ws[kind][dev];
   if (w.bytes < bytes) {
     if (w.ptr) {
       // the old buffer may still be in use by enqueued work
@@ -69,6 +72,35 @@ int workspace(size_t bytes, void** out) {
     w.bytes = bytes;
   }
   *out = w.ptr;
+  return ATTN_OK;
+}
+
+// Split-KV plan.  The key axis is cut into `splits` ranges of `split_keys`
+// keys (a multiple of the 64-key tile); the last range may be shorter, none
+// is empty.  num_splits > 0 asks for that many (fewer when Sk has fewer
+// 64-key tiles); num_splits == 0 picks enough to give the chip about four
+// 128-row workgroups per CU (two resident at a time), without cutting a range
+// below 256 keys.
+constexpr int kMaxSplits = 256;
+constexpr int kSplitBlockM = 128;   // query rows per workgroup of the split kernel
+int split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits, int* split_keys) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
+  const long long tiles = (long long)B * Hq * ((Sq + kSplitBlockM - 1) / kSplitBlockM);
+  const int kt = (Sk + 63) / 64;   // 64-key tiles
+  int want = num_splits;
+  if (want == 0) {
+    constexpr long long kTarget = 4 * 256;
+    const long long by_tiles = (kTarget + tiles - 1) / tiles;
+    const int by_keys = (Sk + 255) / 256;
+    want = (int)(by_tiles < by_keys ? by_tiles : by_keys);
+    if (want > 64) want = 64;
+    if (want < 1) want = 1;
+  }
+  if (want > kt) want = kt;
+  const int per = (kt + want - 1) / want;   // tiles per range
+  *split_keys = per * 64;
+  *splits = (Sk + per * 64 - 1) / (per * 64);
+  if (tiles * *splits > kMax32) return ATTN_ERR_SIZE;
   return ATTN_OK;
 }
 
@@ -204,7 +236,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     const size_t sq_b = al(sizeof(float) * B * Hq * nbq), sk_b = al(sizeof(float) * B * Hkv * nbk);
     const size_t total = al(qb) + 2 * al(kb) + sq_b + 2 * sk_b;
     void* ws = nullptr;
-    rc = workspace(total, &ws);
+    rc = workspace(kWsFp8, total, &ws);
     if (rc) return rc;
     uint8_t* base = (uint8_t*)ws;
     uint8_t* q8 = base;
@@ -275,17 +307,96 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+int attn_split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits_out,
+                    int* split_keys_out) {
+  if (!splits_out || !split_keys_out) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || Sk <= 0) return ATTN_ERR_SHAPE;
+  return split_plan(B, Hq, Sq, Sk, num_splits, splits_out, split_keys_out);
+}
+
+int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse, int splits, int B,
+                 int Hq, int Sq, int d, int dtype, void* stream) {
+  if (!o_part || !lse_part || !o) return ATTN_ERR_NULL;
+  if (splits <= 0 || B <= 0 || Hq <= 0 || Sq <= 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if ((long long)B * Sq * Hq * (d / 4) > kMax32 * 64LL) return ATTN_ERR_SIZE;
+  attn::CombineParams p{};
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.o = o;
+  p.lse = lse;
+  p.splits = splits;
+  p.B = B;
+  p.Hq = Hq;
+  p.Sq = Sq;
+  p.d = d;
+  hipError_t e = attn::launch_combine(p, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                     int Hkv, int Sq, int Sk, int d, float scale, int causal, int num_splits, int dtype,
+                     void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  int splits = 0, split_keys = 0;
+  rc = split_plan(B, Hq, Sq, Sk, num_splits, &splits, &split_keys);
+  if (rc) return rc;
+  if (splits == 1)   // one range: the plain forward computes the same thing
+    return attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, nullptr, dtype, stream);
+  const size_t rows = (size_t)B * Sq * Hq;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t ob = al(sizeof(float) * splits * rows * d), lb = al(sizeof(float) * splits * rows);
+  void* ws = nullptr;
+  rc = workspace(kWsSplit, ob + lb, &ws);
+  if (rc) return rc;
+  attn::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.group = Hq / Hkv;
+  p.q_tok_stride = Hq * d;
+  p.kv_tok_stride = Hkv * d;
+  p.q_batch_stride = (long long)Sq * Hq * d;
+  p.kv_batch_stride = (long long)Sk * Hkv * d;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal);
+  p.splits = splits;
+  p.split_keys = split_keys;
+  p.o_part = (float*)ws;
+  p.lse_part = (float*)((uint8_t*)ws + ob);
+  p.grid = p.tm.ntiles * splits;
+  hipError_t e = attn::launch_fwd_split(p, dtype, d, causal, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return attn_combine(p.o_part, p.lse_part, o, lse, splits, B, Hq, Sq, d, dtype, stream);
+}
+
 void attn_release(void) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return;
   for (int dev = 0; dev < kMaxDevices; ++dev) {
-    if (!g_ws[dev].ptr && !g_signs[dev]) continue;
+    bool any = g_signs[dev] != nullptr;
+    for (int k = 0; k < kWsKinds; ++k) any = any || g_ws[k][dev].ptr != nullptr;
+    if (!any) continue;
     if (hipSetDevice(dev) != hipSuccess) continue;
     (void)hipDeviceSynchronize();
-    if (g_ws[dev].ptr) (void)hipFree(g_ws[dev].ptr);
+    for (int k = 0; k < kWsKinds; ++k) {
+      if (g_ws[k][dev].ptr) (void)hipFree(g_ws[k][dev].ptr);
+      g_ws[k][dev] = Workspace{};
+    }
     if (g_signs[dev]) (void)hipFree(g_signs[dev]);
-    g_ws[dev] = Workspace{};
     g_signs[dev] = nullptr;
   }
   (void)hipSetDevice(cur);

@@ -59,7 +59,12 @@ namespace attn {
 // workgroups share a CU and their waves interleave freely.  NW == 8: one
 // workgroup per CU, two waves per SIMD (wave w and w + 4), run as two groups
 // offset by half a tile (ping-pong, below).
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN>
+// SPLIT: the key axis is cut into p.splits ranges of p.split_keys keys and
+// workgroup split * ntiles + tile writes the fp32 partial result of its range
+// to p.o_part / p.lse_part (flash-decoding; merged by combine_kernel).  The
+// split index is the slow one, so the tile order within a split -- and its
+// placement of K/V groups on XCDs -- is the plain forward's.
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -122,12 +127,21 @@ fwd_kernel(FwdParams p) {
     kv_off = (long long)start * p.kv_tok_stride;
     lse_off = (long long)hq * p.Sq + start;
   } else {
-    tile_decode(p.tm, blockIdx.x, b, hq, mblk);
+    tile_decode(p.tm, SPLIT ? (int)(blockIdx.x % p.tm.ntiles) : (int)blockIdx.x, b, hq, mblk);
     q_len = p.Sq;
     kv_len = p.Sk;
     q_off = (long long)b * p.q_batch_stride;
     kv_off = (long long)b * p.kv_batch_stride;
     lse_off = ((long long)b * p.Hq + hq) * p.Sq;
+  }
+  // key range of a split: keys [key0, key0 + kv_len) of the sequence; K/V
+  // are addressed from key0, causal comparisons stay in sequence positions
+  const int split = SPLIT ? (int)(blockIdx.x / p.tm.ntiles) : 0;
+  const int key0 = split * (SPLIT ? p.split_keys : 0);
+  if constexpr (SPLIT) {
+    kv_len = min(kv_len - key0, p.split_keys);
+    if (kv_len < 0) kv_len = 0;
+    kv_off += (long long)key0 * p.kv_tok_stride;
   }
   const int hkv = hq / p.group;
   const T* Qp = (const T*)p.q + q_off + hq * D;
@@ -139,8 +153,9 @@ fwd_kernel(FwdParams p) {
 
   const int q0 = mblk * BM;
   const int qw = q0 + wave * 32;                       // first query row of this wave
+  const int cw = qw - key0;                            // its causal position relative to the first key
   const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;  // one past the block's last row
-  const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
+  const int kv_end = CAUSAL ? max(0, min(kv_len, q_hi - key0)) : kv_len;
   const int ntile = (kv_end + BN - 1) / BN;
 
   // ---------------------------------------------------------------- Q fragment
@@ -274,14 +289,14 @@ fwd_kernel(FwdParams p) {
   // mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
   auto mask = [&](int t, f32x16 (&sn)[NB]) {
     const int j0 = t * BN;
-    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
+    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > cw);
     if (edge) {
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * bb + 16 * (i >> 3) + 8 * h + (i & 7);
-          const bool dead = (key >= kv_len) || (CAUSAL && key > qi);
+          const bool dead = (key >= kv_len) || (CAUSAL && key > qi - key0);
           sn[bb][i] = dead ? NEG_INF : sn[bb][i];
         }
     }
@@ -428,8 +443,9 @@ fwd_kernel(FwdParams p) {
     if (has_next) finish_max(mx);
   };
 
-  // tiles this wave computes (a causal wave stops at its diagonal)
-  const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
+  // tiles this wave computes (a causal wave stops at its diagonal; a wave
+  // whose rows see no key still runs one fully masked tile)
+  const int n_w = CAUSAL ? min(ntile, max(cw + 31, 0) / BN + 1) : ntile;
 
   // Round r (r = 0 .. ntile) precedes tile r-1's work (and the first tile's
   // S).  Two stages: wait for all copies, barrier, start K_{r+1} and V_r into
@@ -493,7 +509,27 @@ fwd_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + wave_half_swap(l_run);
-  if (qi < q_len) {
+  if (SPLIT && qi < q_len) {
+    // fp32 partial of this key range: O_p = sum P V / l_p, LSE_p
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const long long plane = (long long)split * p.B * p.Sq * p.Hq;
+    float* orow = p.o_part + (plane * D + q_off + (long long)qi * qs + hq * D);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 w;
+        w.x = o[db][4 * g] * inv;
+        w.y = o[db][4 * g + 1] * inv;
+        w.z = o[db][4 * g + 2] * inv;
+        w.w = o[db][4 * g + 3] * inv;
+        *(float4*)(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (h == 0) {
+      const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+      p.lse_part[plane + lse_off + qi] = lse;
+    }
+  } else if (qi < q_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     T* orow = Op + (long long)qi * qs;
 #pragma unroll
@@ -520,14 +556,25 @@ constexpr int fwd_lds_bytes() {
   return 2 * (NW == 8 ? 3 : 2) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
 }
 
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   constexpr int lds = fwd_lds_bytes<D, BN, NW>();
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      (const void*)fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN>), dim3(p.grid), dim3(64 * NW), lds, s, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT>), dim3(p.grid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
+}
+
+// Split-KV partials: 4-wave (128-row) blocks, dense inputs
+template <typename T, int D>
+static hipError_t launch_split_t(const FwdParams& p, int causal, hipStream_t s) {
+  return causal ? launch_one<T, D, 64, 4, true, false, true>(p, s) : launch_one<T, D, 64, 4, false, false, true>(p, s);
+}
+
+hipError_t launch_fwd_split(const FwdParams& p, int dtype, int d, int causal, hipStream_t s) {
+  if (dtype == 0) return d == 128 ? launch_split_t<__bf16, 128>(p, causal, s) : launch_split_t<__bf16, 64>(p, causal, s);
+  return d == 128 ? launch_split_t<_Float16, 128>(p, causal, s) : launch_split_t<_Float16, 64>(p, causal, s);
 }
 
 template <typename T, int D, int BN, int NW>

@@ -27,6 +27,19 @@ struct FwdParams {
   float scale_log2;           // scale * log2(e)
   TileMap tm;                 // dense tile order
   int grid;                   // workgroups launched
+  // split-KV partials (launch_fwd_split): key ranges of split_keys keys
+  int splits = 1;
+  int split_keys = 0;
+  float* o_part = nullptr;    // [splits, B, Sq, Hq, D] fp32
+  float* lse_part = nullptr;  // [splits, B, Hq, Sq] fp32
+};
+
+struct CombineParams {
+  const float* o_part;        // [splits, B, Sq, Hq, d]
+  const float* lse_part;      // [splits, B, Hq, Sq]
+  void* o;                    // [B, Sq, Hq, d] in the output type
+  float* lse;                 // [B, Hq, Sq] or nullptr
+  int splits, B, Hq, Sq, d;
 };
 
 struct Fp8FwdParams {
@@ -63,6 +76,11 @@ int fwd_fp8_block_m();
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
 // d = 128 dense bf16/fp16 with 256-row blocks, one wave per SIMD.
 hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s);
+// Split-KV partials with the 4-wave kernel (dense, d in {64, 128}); grid =
+// splits x tiles, split index slowest.
+hipError_t launch_fwd_split(const FwdParams& p, int dtype, int d, int causal, hipStream_t s);
+// Merge of split-KV partials into O (dtype 0 bf16, 1 fp16) and LSE.
+hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);
 

@@ -138,6 +138,60 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                  void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
                  float scale, int causal, void* stream);
 
+/*
+ * attn_fwd_splitkv -- the dense bf16/fp16 forward of attn_fwd with the key
+ * axis cut into ranges (split-KV, "flash-decoding": the Hopper tag page,
+ * l1-ca0.github.io, contents 10 and 10.2.1).  Each (query tile, key range)
+ * pair is one workgroup that writes the normalised partial output O_p of its
+ * range and its log-sum-exp LSE_p in fp32; attn_combine then merges the
+ * ranges (block-combine of the streaming softmax, same page, contents 3.2.1).
+ * The result equals attn_fwd's up to rounding.  It pays off when the tiles
+ * of the plain forward are too few to fill the device: few query rows
+ * (decoding), few heads, long keys.
+ *
+ * Arguments, layouts and causal semantics as for attn_fwd (dense only, no
+ * cu_seqlens); dtype ATTN_BF16 or ATTN_FP16.
+ * num_splits: the number of key ranges wanted (0 = chosen by the library,
+ *   see attn_split_plan; at most 256).  The plan rounds range lengths up to
+ *   multiples of 64 keys, so fewer ranges may result; with one range the
+ *   call is attn_fwd.
+ * The partials live in a library-owned, lazily grown device workspace
+ * (splits * B * Sq * Hq * (d + 1) floats; released by attn_release).  Calls
+ * on different streams of one device share it and must not overlap.
+ * lse may be NULL.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     int num_splits, int dtype, void* stream);
+
+/*
+ * attn_split_plan -- the key ranges attn_fwd_splitkv uses: writes the number
+ * of ranges and the keys per range (a multiple of 64; the last range holds
+ * the rest, no range is empty).  num_splits == 0 picks enough ranges for
+ * about 1024 workgroups of 128 query rows, each range >= 256 keys, at most
+ * 64 ranges.  Returns ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_ARG
+ * (num_splits < 0 or > 256) or ATTN_ERR_SIZE.
+ */
+int attn_split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits_out,
+                    int* split_keys_out);
+
+/*
+ * attn_combine -- merge of split-KV partials (the Hopper tag page,
+ * contents 10.2.1, with the block-combine of contents 3.2.1):
+ *   m = max_p LSE_p,  w_p = exp(LSE_p - m),
+ *   LSE = m + log sum_p w_p,  O = sum_p w_p O_p / sum_p w_p.
+ * A partial with LSE_p = -inf (its range held no visible key) contributes
+ * nothing; a row whose partials are all -inf gets O = 0 and LSE = -inf.
+ *   o_part   [splits, B, Sq, Hq, d] fp32, each O_p already normalised,
+ *   lse_part [splits, B, Hq, Sq] fp32 (natural log, scale included),
+ *   o        [B, Sq, Hq, d] in dtype (ATTN_BF16 / ATTN_FP16), rounded to
+ *            nearest even,
+ *   lse      [B, Hq, Sq] fp32, may be NULL.
+ * All device pointers, caller-owned.  d must be 64 or 128.
+ */
+int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse, int splits,
+                 int B, int Hq, int Sq, int d, int dtype, void* stream);
+
 /* The library's default Hadamard sign vector used by ATTN_FP8_E4M3_HADAMARD:
  * writes n (<= 128) host floats of +-1, sign i being the top bit of the
  * splitmix64 output for counter (55 << 32) + i + 1.  Returns ATTN_OK, or
@@ -157,7 +211,8 @@ int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* 
 /* Human-readable text for a status code. */
 const char* attn_strerror(int code);
 
-/* Frees the library's fp8 workspace on every device that has one. */
+/* Frees the library's workspaces (fp8 operands, split-KV partials) on every
+ * device that has them. */
 void attn_release(void);
 
 #ifdef __cplusplus

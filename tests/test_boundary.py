@@ -110,3 +110,54 @@ def test_tile_of_rejects_bad_args(lib):
         ea.tile_of(10**6, 1, 2, 2, 256, 128, False)
     with pytest.raises(ea.AttnError):
         ea.tile_of(0, 1, 3, 2, 256, 128, False)
+
+
+@pytest.mark.parametrize("B,Hq,Sq,Sk,n", [
+    (4, 32, 1, 16384, 0), (1, 1, 1, 100, 0), (2, 8, 300, 5000, 0), (1, 2, 256, 1000, 3),
+    (1, 2, 256, 100, 7), (1, 2, 256, 129, 3), (1, 1, 1, 64, 256), (16, 64, 4096, 4096, 0),
+])
+def test_split_plan_covers_keys(lib, B, Hq, Sq, Sk, n):
+    splits, keys = ea.split_plan(B, Hq, Sq, Sk, n)
+    assert keys % 64 == 0 and keys > 0
+    # every range non-empty, together exactly [0, Sk)
+    assert (splits - 1) * keys < Sk <= splits * keys
+    if n > 0:
+        assert splits <= n
+    else:
+        assert 1 <= splits <= 64
+        tiles = B * Hq * ((Sq + 127) // 128)
+        if splits > 1:
+            assert keys >= 256 or Sk < 512
+            assert tiles * (splits - 1) < 1024
+
+
+def test_split_plan_auto_decode_shape(lib):
+    # 128 tiles of one query row each -> 8 ranges of 2048 keys
+    assert ea.split_plan(4, 32, 1, 16384, 0) == (8, 2048)
+    # enough tiles already -> one range
+    assert ea.split_plan(2, 32, 8192, 8192, 0)[0] == 1
+
+
+def test_splitkv_and_combine_validate(lib):
+    def sk(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=64, Sk=256, d=64,
+                 scale=0.125, causal=0, n=2, dtype=0)
+        a.update(kw)
+        return lib.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                    a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["n"], a["dtype"],
+                                    None)
+    assert sk(k=None) == -1
+    assert sk(Sk=0) == -2
+    assert sk(d=96) == -3
+    assert sk(Hq=3) == -4
+    assert sk(dtype=2) == -5 and sk(dtype=3) == -5
+    assert sk(scale=float("nan")) == -6
+    assert sk(n=-1) == -6 and sk(n=257) == -6
+    c = lambda **kw: lib.attn_combine(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("o", FAKE), None,
+                                      kw.get("P", 2), kw.get("B", 1), 2, kw.get("Sq", 8), kw.get("d", 64),
+                                      kw.get("dtype", 0), None)
+    assert c(op=None) == -1 and c(o=None) == -1
+    assert c(P=0) == -2 and c(Sq=0) == -2
+    assert c(d=32) == -3
+    assert c(dtype=2) == -5
+    assert lib.attn_split_plan(1, 1, 1, 1, 0, None, None) == -1
