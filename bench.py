@@ -4,7 +4,9 @@
 
 One step is one pass of the hot path over one batch of the workload: for the
 bf16/fp16 workloads one ``attn_fwd`` call; for the fp8 workloads the fp8
-prepass of Q, K and V plus the fp8 attention kernel.  Inputs are resident in
+prepass of Q, K and V plus the fp8 attention kernel; for the split-KV leg
+(decode shape) one ``attn_fwd_splitkv`` call, i.e. the split kernel and the
+combine kernel.  Inputs are resident in
 device memory before the timed region.  The timed region is bracketed by
 ``torch.cuda.synchronize()`` and measured with HIP events on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
@@ -30,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16, fp8) and % of MFMA peak, 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0                                            # MI355X HBM3E
 _FWD_SOURCES = ("exact_attention_75_amd/csrc/attn_fwd.hip", "exact_attention_75_amd/csrc/attn_fwd_wide.hip",
                 "exact_attention_75_amd/csrc/wide_regs.h", "exact_attention_75_amd/csrc/kernel_common.h")
 KERNEL_SOURCES = {"bf16": _FWD_SOURCES, "fp16": _FWD_SOURCES,
@@ -46,6 +49,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workloads")
+    ap.add_argument("--no-split", action="store_true", help="skip the split-KV decode leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for the HBM byte counters)")
@@ -148,6 +152,45 @@ def fp8_leg(ea, name, steps, warmup, hadamard=False):
             "kernel_pct_of_fp8_peak": round(100 * fl / (ms_k * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2),
             "step_ms_with_prepass": round(ms_full, 5),
             "step_tflops_with_prepass": round(fl / (ms_full * 1e-3) / 1e12, 2)}
+
+
+def splitkv_leg(ea, name, steps, warmup):
+    """Split-KV on the decode shape: the whole step (split-KV kernel + combine,
+    PackGQA as the library chooses) against the plain forward on the same
+    inputs (which packs too, without splitting the keys).  HBM-bound: the algorithmic
+    bytes are Q, K, V read once and O, LSE written once."""
+    import torch
+    import workloads as W
+    w = W.CONFIGS[name]
+    _, dev = device_inputs(w)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    o = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    L = ea.library()
+    st = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq,
+            w.Sk, w.d, float(w.scale), int(w.causal))
+
+    def split():
+        rc = L.attn_fwd_splitkv(*args, 0, -1, ea.ATTN_BF16, st)
+        if rc != 0:
+            raise RuntimeError(L.attn_strerror(rc).decode())
+
+    def plain():
+        rc = L.attn_fwd(*args, None, ea.ATTN_BF16, st)
+        if rc != 0:
+            raise RuntimeError(L.attn_strerror(rc).decode())
+    ms_s = time_steps(split, steps, warmup) / steps
+    ms_p = time_steps(plain, steps, warmup) / steps
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
+    splits, keys, packed = ea.split_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, d=w.d)
+    gbs = nbytes / (ms_s * 1e-3) / 1e9
+    return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} Sk={w.Sk} d={w.d} bf16 "
+                        f"{'causal' if w.causal else 'full'}",
+            "splits": splits, "split_keys": keys, "pack_gqa": packed,
+            "step_ms": round(ms_s, 5), "plain_fwd_ms": round(ms_p, 5), "speedup_vs_plain": round(ms_p / ms_s, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
 
 def time_steps(step, steps, warmup):
@@ -265,6 +308,8 @@ def main():
         out["fp8"] = {"c3fp8": fp8_leg(ea, "c3fp8", a.steps, a.warmup),
                       "c5": fp8_leg(ea, "c5", max(5, a.steps // 5), 3),
                       "c5_hadamard": fp8_leg(ea, "c5", max(5, a.steps // 5), 3, hadamard=True)}
+    if not a.no_split:
+        out["splitkv"] = splitkv_leg(ea, "dec", max(20, a.steps), a.warmup)
     if a.extra:
         for name in ("c1", "c2", "c4"):
             if name == a.workload:

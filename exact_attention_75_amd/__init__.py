@@ -60,9 +60,9 @@ def library() -> ctypes.CDLL:
     L.attn_tile_of.restype = I
     L.attn_grid_size.argtypes = [I, I, I, I, I, IP, IP]
     L.attn_grid_size.restype = I
-    L.attn_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    L.attn_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, I, P]
     L.attn_fwd_splitkv.restype = I
-    L.attn_split_plan.argtypes = [I, I, I, I, I, IP, IP]
+    L.attn_split_plan.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
     L.attn_split_plan.restype = I
     L.attn_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     L.attn_combine.restype = I
@@ -152,21 +152,27 @@ def _kernel_dtype(*ts) -> int:
     raise ValueError("tensors must all be bf16 or all fp16")
 
 
-def split_plan(B: int, Hq: int, Sq: int, Sk: int, num_splits: int = 0) -> Tuple[int, int]:
-    """(number of key ranges, keys per range) that ``attn_fwd_splitkv`` uses."""
-    n, keys = ctypes.c_int(), ctypes.c_int()
-    _check(library().attn_split_plan(B, Hq, Sq, Sk, num_splits, ctypes.byref(n), ctypes.byref(keys)),
-           "attn_split_plan")
-    return n.value, keys.value
+def _pack_arg(pack_gqa: Optional[bool]) -> int:
+    return -1 if pack_gqa is None else int(bool(pack_gqa))
+
+
+def split_plan(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int = 128, num_splits: int = 0,
+               pack_gqa: Optional[bool] = None) -> Tuple[int, int, bool]:
+    """(number of key ranges, keys per range, packed) that ``attn_fwd_splitkv`` uses."""
+    n, keys, pk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(library().attn_split_plan(B, Hq, Hkv, Sq, Sk, d, num_splits, _pack_arg(pack_gqa), ctypes.byref(n),
+                                     ctypes.byref(keys), ctypes.byref(pk)), "attn_split_plan")
+    return n.value, keys.value, bool(pk.value)
 
 
 def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-                scale: Optional[float] = None, num_splits: int = 0,
+                scale: Optional[float] = None, num_splits: int = 0, pack_gqa: Optional[bool] = None,
                 return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Dense bf16/fp16 forward with the key axis split (``attn_fwd_splitkv``).
 
     q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> o [B, Sq, Hq, d], lse [B, Hq, Sq].
-    num_splits 0 lets the library choose (``split_plan``)."""
+    num_splits 0 lets the library choose (``split_plan``); pack_gqa None is
+    the automatic PackGQA choice, True / False force it."""
     _need_gpu(q, k, v)
     dt = _kernel_dtype(q, k, v)
     B, Sq, Hq, d = q.shape
@@ -176,7 +182,8 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     rc = library().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
-                                    float(scale), int(bool(causal)), int(num_splits), dt, _stream())
+                                    float(scale), int(bool(causal)), int(num_splits), _pack_arg(pack_gqa), dt,
+                                    _stream())
     _check(rc, "attn_fwd_splitkv")
     return o, lse
 

@@ -75,26 +75,63 @@ int workspace(int kind, size_t bytes, void** out) {
   return ATTN_OK;
 }
 
-// Split-KV plan.  The key axis is cut into `splits` ranges of `split_keys`
-// keys (a multiple of the 64-key tile); the last range may be shorter, none
-// is empty.  num_splits > 0 asks for that many (fewer when Sk has fewer
-// 64-key tiles); num_splits == 0 picks enough to give the chip about four
-// 128-row workgroups per CU (two resident at a time), without cutting a range
-// below 256 keys.
-constexpr int kMaxSplits = 256;
-constexpr int kSplitBlockM = 128;   // query rows per workgroup of the split kernel
-int split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits, int* split_keys) {
+constexpr int kMaxSplits = attn::kCombineMaxSplits;
+constexpr int kSplitBlockM = 128;   // query rows per workgroup of the split / packed kernel
+// PackGQA (one tile holds the rows of every query head of a KV group) needs
+// the group size to divide the 128-row block.  Automatic choice: pack when it
+// gives strictly fewer 128-row tiles, i.e. when the unpacked tiles would be
+// mostly empty (few query positions, as in decoding).
+bool pack_allowed(int Hq, int Hkv) {
+  const int g = Hq / Hkv;
+  return g > 1 && kSplitBlockM % g == 0;
+}
+int pack_choice(int pack_gqa, int Hq, int Hkv, int Sq, int* pack) {
+  const int g = Hq / Hkv;
+  if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_ARG;
+  if (pack_gqa == 1 && g > 1 && !pack_allowed(Hq, Hkv)) return ATTN_ERR_ARG;
+  if (pack_gqa == -1) {
+    const long long packed = ((long long)Sq * g + kSplitBlockM - 1) / kSplitBlockM;
+    const long long unpacked = (long long)g * ((Sq + kSplitBlockM - 1) / kSplitBlockM);
+    *pack = pack_allowed(Hq, Hkv) && packed < unpacked;
+  } else {
+    *pack = pack_gqa == 1 && g > 1;
+  }
+  return ATTN_OK;
+}
+// 128-row tiles of a dense problem, packed or not
+long long dense_tiles(int B, int Hq, int Hkv, int Sq, int pack) {
+  if (pack) return (long long)B * Hkv * (((long long)Sq * (Hq / Hkv) + kSplitBlockM - 1) / kSplitBlockM);
+  return (long long)B * Hq * ((Sq + kSplitBlockM - 1) / kSplitBlockM);
+}
+
+// Split-KV plan over `tiles` 128-row tiles.  The key axis is cut into
+// `splits` ranges of `split_keys` keys (a multiple of the 64-key tile); the
+// last range may be shorter, none is empty.  num_splits > 0 asks for that
+// many (fewer when Sk has fewer 64-key tiles).  num_splits == 0 models the
+// time as (waves of workgroups over the device's resident slots) x (work of
+// one workgroup: its share of the keys plus a fixed cost worth 128 keys) and
+// takes the cheapest count, the smallest on ties, with ranges of at least
+// 256 keys and at most 64 ranges.  Slots: 256 CUs (MI355X) times the
+// workgroups of the 4-wave kernel one CU holds (one with d = 128, whose K/V
+// ring and Q block take 96 KiB of LDS; two with d = 64).
+int split_plan(long long tiles, int Sk, int d, int num_splits, int* splits, int* split_keys) {
   if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
-  const long long tiles = (long long)B * Hq * ((Sq + kSplitBlockM - 1) / kSplitBlockM);
   const int kt = (Sk + 63) / 64;   // 64-key tiles
   int want = num_splits;
   if (want == 0) {
-    constexpr long long kTarget = 4 * 256;
-    const long long by_tiles = (kTarget + tiles - 1) / tiles;
-    const int by_keys = (Sk + 255) / 256;
-    want = (int)(by_tiles < by_keys ? by_tiles : by_keys);
-    if (want > 64) want = 64;
-    if (want < 1) want = 1;
+    const long long slots = 256LL * (d == 128 ? 1 : 2);
+    int cap = (Sk + 255) / 256;
+    if (cap > 64) cap = 64;
+    want = 1;
+    double best = 0.0;
+    for (int n = 1; n <= cap; ++n) {
+      const long long waves = (tiles * n + slots - 1) / slots;
+      const double cost = (double)waves * ((double)Sk / n + 128.0);
+      if (n == 1 || cost < best) {
+        best = cost;
+        want = n;
+      }
+    }
   }
   if (want > kt) want = kt;
   const int per = (kt + want - 1) / want;   // tiles per range
@@ -113,6 +150,59 @@ uint64_t splitmix64(uint64_t x) {
 
 // device copy of the default sign vector, per device
 float* g_signs[kMaxDevices] = {};
+
+void fill_params(attn::FwdParams& p, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.group = Hq / Hkv;
+  p.q_tok_stride = Hq * d;
+  p.kv_tok_stride = Hkv * d;
+  p.q_batch_stride = (long long)Sq * Hq * d;
+  p.kv_batch_stride = (long long)Sk * Hkv * d;
+  p.scale_log2 = scale * 1.4426950408889634f;
+}
+
+// Dense bf16/fp16 forward after validation: the plain kernels (splits == 1)
+// or split-KV partials and their combine, with or without PackGQA.
+int fwd16_dense(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
+                int Sk, int d, float scale, int causal, int pack, int splits, int split_keys, int dtype,
+                hipStream_t s) {
+  attn::FwdParams p{};
+  fill_params(p, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale);
+  p.pack = pack;
+  const int g = Hq / Hkv;
+  const int bm = (pack || splits > 1) ? kSplitBlockM : attn::fwd_block_m(dtype, d, 0);
+  p.tm = pack ? attn::make_tile_map(B, Hkv, Hkv, Sq * g, bm, causal) : attn::make_tile_map(B, Hq, Hkv, Sq, bm, causal);
+  if (splits <= 1) {
+    p.grid = p.tm.ntiles;
+    hipError_t e = attn::launch_fwd(p, dtype, d, causal, 0, s);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e);
+  }
+  const size_t rows = (size_t)B * Sq * Hq;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t ob = al(sizeof(float) * splits * rows * d), lb = al(sizeof(float) * splits * rows);
+  void* ws = nullptr;
+  int rc = workspace(kWsSplit, ob + lb, &ws);
+  if (rc) return rc;
+  p.splits = splits;
+  p.split_keys = split_keys;
+  p.o_part = (float*)ws;
+  p.lse_part = (float*)((uint8_t*)ws + ob);
+  p.grid = p.tm.ntiles * splits;
+  hipError_t e = attn::launch_fwd_split(p, dtype, d, causal, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return attn_combine(p.o_part, p.lse_part, o, lse, splits, B, Hq, Sq, d, dtype, s);
+}
 
 }  // namespace
 
@@ -274,50 +364,41 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return rc;
   }
 
-  attn::FwdParams p{};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.cu_seqlens = cu_seqlens;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.Sq = Sq;
-  p.Sk = Sk;
-  p.group = Hq / Hkv;
-  p.q_tok_stride = Hq * d;
-  p.kv_tok_stride = Hkv * d;
-  p.q_batch_stride = (long long)Sq * Hq * d;
-  p.kv_batch_stride = (long long)Sk * Hkv * d;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  if (varlen) {
-    // one tile per (head, query block of a sequence); the number of blocks is
-    // at most ceil(T / BM) + (number of sequences), the rest exit at once
-    const int bm = attn::fwd_block_m(dtype, d, 1);
-    const long long nb = (Sq + bm - 1) / bm + B;
-    if (nb * Hq > kMax32) return ATTN_ERR_SIZE;
-    p.grid = (int)(nb * Hq);
-  } else {
-    p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_block_m(dtype, d, 0), causal);
-    p.grid = p.tm.ntiles;
+  if (!varlen) {
+    int pack = 0;
+    rc = pack_choice(-1, Hq, Hkv, Sq, &pack);
+    if (rc) return rc;
+    return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, 1, 0, dtype, s);
   }
-  hipError_t e = attn::launch_fwd(p, dtype, d, causal, varlen ? 1 : 0, s);
+  attn::FwdParams p{};
+  fill_params(p, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale);
+  p.cu_seqlens = cu_seqlens;
+  // one tile per (head, query block of a sequence); the number of blocks is
+  // at most ceil(T / BM) + (number of sequences), the rest exit at once
+  const int bm = attn::fwd_block_m(dtype, d, 1);
+  const long long nb = (Sq + bm - 1) / bm + B;
+  if (nb * Hq > kMax32) return ATTN_ERR_SIZE;
+  p.grid = (int)(nb * Hq);
+  hipError_t e = attn::launch_fwd(p, dtype, d, causal, 1, s);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
-int attn_split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits_out,
-                    int* split_keys_out) {
-  if (!splits_out || !split_keys_out) return ATTN_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Sq <= 0 || Sk <= 0) return ATTN_ERR_SHAPE;
-  return split_plan(B, Hq, Sq, Sk, num_splits, splits_out, split_keys_out);
+int attn_split_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits, int pack_gqa, int* splits_out,
+                    int* split_keys_out, int* pack_out) {
+  if (!splits_out || !split_keys_out || !pack_out) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (Hq % Hkv) return ATTN_ERR_GQA;
+  int rc = pack_choice(pack_gqa, Hq, Hkv, Sq, pack_out);
+  if (rc) return rc;
+  return split_plan(dense_tiles(B, Hq, Hkv, Sq, *pack_out), Sk, d, num_splits, splits_out, split_keys_out);
 }
 
 int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse, int splits, int B,
                  int Hq, int Sq, int d, int dtype, void* stream) {
   if (!o_part || !lse_part || !o) return ATTN_ERR_NULL;
   if (splits <= 0 || B <= 0 || Hq <= 0 || Sq <= 0) return ATTN_ERR_SHAPE;
+  if (splits > attn::kCombineMaxSplits) return ATTN_ERR_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
   if ((long long)B * Sq * Hq * (d / 4) > kMax32 * 64LL) return ATTN_ERR_SIZE;
@@ -336,50 +417,19 @@ int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                     int Hkv, int Sq, int Sk, int d, float scale, int causal, int num_splits, int dtype,
-                     void* stream) {
+                     int Hkv, int Sq, int Sk, int d, float scale, int causal, int num_splits, int pack_gqa,
+                     int dtype, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
   int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
   if (rc) return rc;
-  int splits = 0, split_keys = 0;
-  rc = split_plan(B, Hq, Sq, Sk, num_splits, &splits, &split_keys);
+  int pack = 0, splits = 0, split_keys = 0;
+  rc = pack_choice(pack_gqa, Hq, Hkv, Sq, &pack);
   if (rc) return rc;
-  if (splits == 1)   // one range: the plain forward computes the same thing
-    return attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, nullptr, dtype, stream);
-  const size_t rows = (size_t)B * Sq * Hq;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t ob = al(sizeof(float) * splits * rows * d), lb = al(sizeof(float) * splits * rows);
-  void* ws = nullptr;
-  rc = workspace(kWsSplit, ob + lb, &ws);
+  rc = split_plan(dense_tiles(B, Hq, Hkv, Sq, pack), Sk, d, num_splits, &splits, &split_keys);
   if (rc) return rc;
-  attn::FwdParams p{};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.cu_seqlens = nullptr;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.Sq = Sq;
-  p.Sk = Sk;
-  p.group = Hq / Hkv;
-  p.q_tok_stride = Hq * d;
-  p.kv_tok_stride = Hkv * d;
-  p.q_batch_stride = (long long)Sq * Hq * d;
-  p.kv_batch_stride = (long long)Sk * Hkv * d;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal);
-  p.splits = splits;
-  p.split_keys = split_keys;
-  p.o_part = (float*)ws;
-  p.lse_part = (float*)((uint8_t*)ws + ob);
-  p.grid = p.tm.ntiles * splits;
-  hipError_t e = attn::launch_fwd_split(p, dtype, d, causal, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e);
-  return attn_combine(p.o_part, p.lse_part, o, lse, splits, B, Hq, Sq, d, dtype, stream);
+  return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, splits, split_keys, dtype,
+                     (hipStream_t)stream);
 }
 
 void attn_release(void) {

@@ -8,12 +8,18 @@
 //     m = max_s LSE_s,  w_s = exp(LSE_s - m),  LSE = m + log sum_s w_s,
 //     O = sum_s w_s O_s / sum_s w_s
 //
-// A split that saw no key of a row has LSE_s = -inf and contributes nothing;
-// a row with no key at all gets O = 0 and LSE = -inf.
+// A split that saw no key of a row has LSE_s = -inf and contributes nothing
+// (its O_s is never used, whatever it holds); a row with no key at all gets
+// O = 0 and LSE = -inf.
 //
-// HBM-bound: one thread per (row, 4 channels) reads the splits' LSE values
-// (the same few floats for all threads of a row, served from cache) and its
-// 16 bytes of every partial, and writes 4 output elements.
+// HBM-bound and short: the partials of a decode step are a few MiB, so the
+// kernel is built for memory-level parallelism rather than for many rows.
+// D/4 consecutive threads own one row (4 channels each).  They read the row's
+// LSE values with a stride of D/4 splits, reduce max and sum across the row's
+// lanes with shuffles, and leave the weights in LDS; then every thread sums
+// its 4 channels over all splits with unconditional, unrolled loads (a weight
+// of 0 selects nothing, so the loads need no branch and stay in flight
+// together).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -22,39 +28,67 @@
 
 namespace attn {
 
-template <typename T>
+template <int W>
+__device__ __forceinline__ float row_max(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, W));
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, W);
+  return x;
+}
+
+template <typename T, int D>
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
-  const int c4n = p.d / 4;
+  constexpr int TPR = D / 4;        // threads per row
+  constexpr int RPB = 256 / TPR;    // rows per workgroup
+  constexpr float NEG_INF = -__builtin_inff();
+  __shared__ float wsh[RPB][kCombineMaxSplits];
+
+  const int t = threadIdx.x % TPR;
+  const int rl = threadIdx.x / TPR;
   const long long rows = (long long)p.B * p.Sq * p.Hq;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= rows * c4n) return;
-  const long long row = idx / c4n;          // token-major row: (b * Sq + i) * Hq + h
-  const int c4 = (int)(idx % c4n);
-  const int hq = (int)(row % p.Hq);
-  const long long bi = row / p.Hq;
+  const long long row = (long long)blockIdx.x * RPB + rl;   // token-major: (b * Sq + i) * Hq + h
+  const bool valid = row < rows;
+  const long long r = valid ? row : rows - 1;               // keeps every address in bounds
+  const int hq = (int)(r % p.Hq);
+  const long long bi = r / p.Hq;
   const int i = (int)(bi % p.Sq);
   const int b = (int)(bi / p.Sq);
   const long long lse_idx = ((long long)b * p.Hq + hq) * p.Sq + i;
-  const long long lplane = rows;            // LSE values per split
-  const long long oplane = rows * p.d;      // O values per split
+  const long long lplane = rows;        // LSE values per split
+  const long long oplane = rows * D;    // O values per split
 
-  float m = -__builtin_inff();
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.lse_part[s * lplane + lse_idx]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float m = NEG_INF;
+  for (int s = t; s < p.splits; s += TPR) m = fmaxf(m, p.lse_part[s * lplane + lse_idx]);
+  m = row_max<TPR>(m);
+  const float m_safe = (m == NEG_INF) ? 0.f : m;
   float wsum = 0.f;
-  if (m != -__builtin_inff()) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float ls = p.lse_part[s * lplane + lse_idx];
-      if (ls == -__builtin_inff()) continue;
-      const float w = expf(ls - m);
-      const float4 v = *(const float4*)(p.o_part + s * oplane + row * p.d + 4 * c4);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
-      wsum += w;
-    }
+  for (int s = t; s < p.splits; s += TPR) {
+    const float ls = p.lse_part[s * lplane + lse_idx];
+    const float w = (ls == NEG_INF) ? 0.f : expf(ls - m_safe);
+    wsh[rl][s] = w;
+    wsum += w;
   }
+  wsum = row_sum<TPR>(wsum);
+  __syncthreads();
+
+  const float* op = p.o_part + r * D + 4 * t;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) {
+    const float4 v = *(const float4*)(op + s * oplane);
+    const float w = wsh[rl][s];
+    const bool use = w != 0.f;
+    acc.x += use ? w * v.x : 0.f;
+    acc.y += use ? w * v.y : 0.f;
+    acc.z += use ? w * v.z : 0.f;
+    acc.w += use ? w * v.w : 0.f;
+  }
+  if (!valid) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   typedef T T4 __attribute__((ext_vector_type(4)));
   T4 out;
@@ -62,17 +96,23 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
   out[1] = (T)(acc.y * inv);
   out[2] = (T)(acc.z * inv);
   out[3] = (T)(acc.w * inv);
-  *(T4*)((T*)p.o + row * p.d + 4 * c4) = out;
-  if (p.lse != nullptr && c4 == 0) p.lse[lse_idx] = wsum > 0.f ? m + logf(wsum) : -__builtin_inff();
+  *(T4*)((T*)p.o + r * D + 4 * t) = out;
+  if (p.lse != nullptr && t == 0) p.lse[lse_idx] = wsum > 0.f ? m + logf(wsum) : NEG_INF;
+}
+
+template <typename T, int D>
+static hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 4);
+  const long long rows = (long long)p.B * p.Sq * p.Hq;
+  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s) {
-  const long long threads = (long long)p.B * p.Sq * p.Hq * (p.d / 4);
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-  if (grid == 0) return hipSuccess;
-  if (dtype == 0) hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(combine_kernel<_Float16>, dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (dtype == 0) return p.d == 128 ? launch_combine_t<__bf16, 128>(p, s) : launch_combine_t<__bf16, 64>(p, s);
+  return p.d == 128 ? launch_combine_t<_Float16, 128>(p, s) : launch_combine_t<_Float16, 64>(p, s);
 }
 
 }  // namespace attn

@@ -64,7 +64,11 @@ namespace attn {
 // to p.o_part / p.lse_part (flash-decoding; merged by combine_kernel).  The
 // split index is the slow one, so the tile order within a split -- and its
 // placement of K/V groups on XCDs -- is the plain forward's.
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT>
+// PACK (PackGQA, dense only): a tile holds the query rows of all p.group
+// query heads that share one KV head, row r = position * group + head in the
+// group, so that few query positions (decoding) still fill the tile and K/V
+// are fetched once for the group.  The tile map then runs over KV heads.
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT, bool PACK>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -84,6 +88,7 @@ fwd_kernel(FwdParams p) {
   constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(BN == 64 && (BN * CPR) % (NW * 64) == 0, "tile shape");
+  static_assert(!(PACK && VARLEN), "PackGQA is for dense inputs");
 
   // With d = 128 the Q block lives in LDS (its 32 registers per lane are
   // needed by the pipeline); with d = 64 it stays in registers.
@@ -127,7 +132,9 @@ fwd_kernel(FwdParams p) {
     kv_off = (long long)start * p.kv_tok_stride;
     lse_off = (long long)hq * p.Sq + start;
   } else {
+    // with PACK the map runs over KV heads: hq is the KV head here
     tile_decode(p.tm, SPLIT ? (int)(blockIdx.x % p.tm.ntiles) : (int)blockIdx.x, b, hq, mblk);
+    if (PACK) hq *= p.group;   // first query head of the group
     q_len = p.Sq;
     kv_len = p.Sk;
     q_off = (long long)b * p.q_batch_stride;
@@ -144,6 +151,15 @@ fwd_kernel(FwdParams p) {
     kv_off += (long long)key0 * p.kv_tok_stride;
   }
   const int hkv = hq / p.group;
+  // Query rows of the tile: row r is query position row_pos(r) of head
+  // hq + (r % grp); row_off(r) its element offset from Qp / Op.
+  const int grp = PACK ? p.group : 1;
+  const int rows_len = q_len * grp;
+  auto row_pos = [&](int r) { return PACK ? r / grp : r; };
+  auto row_off = [&](int r) -> long long {
+    return PACK ? (long long)(r / grp) * p.q_tok_stride + (r % grp) * D : (long long)r * p.q_tok_stride;
+  };
+  auto lse_idx = [&](int r) -> long long { return PACK ? lse_off + (long long)(r % grp) * p.Sq + r / grp : lse_off + r; };
   const T* Qp = (const T*)p.q + q_off + hq * D;
   const T* Kp = (const T*)p.k + kv_off + hkv * D;
   const T* Vp = (const T*)p.v + kv_off + hkv * D;
@@ -153,8 +169,9 @@ fwd_kernel(FwdParams p) {
 
   const int q0 = mblk * BM;
   const int qw = q0 + wave * 32;                       // first query row of this wave
-  const int cw = qw - key0;                            // its causal position relative to the first key
-  const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;  // one past the block's last row
+  const int cw = row_pos(qw) - key0;                   // its causal position relative to the first key
+  const int cw_hi = row_pos(qw + 31) - key0;           // and that of its last row
+  const int q_hi = min(q_len, row_pos(q0 + BM - 1) + 1);   // one past the block's last position
   const int kv_end = CAUSAL ? max(0, min(kv_len, q_hi - key0)) : kv_len;
   const int ntile = (kv_end + BN - 1) / BN;
 
@@ -164,8 +181,8 @@ fwd_kernel(FwdParams p) {
   constexpr int KTR = QLDS ? 1 : KT;
   vec8 qf[KTR];
   if constexpr (!QLDS) {
-    const int qrow = (qw + qlane < q_len) ? qw + qlane : q_len - 1;
-    const T* qr = Qp + (long long)qrow * qs + 8 * h;
+    const int qrow = (qw + qlane < rows_len) ? qw + qlane : rows_len - 1;
+    const T* qr = Qp + row_off(qrow) + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KT; ++kk) qf[kk] = *(const vec8*)(qr + 16 * kk);
   }
@@ -203,10 +220,13 @@ fwd_kernel(FwdParams p) {
     for (int i = 0; i < QLOADS; ++i) {
       const int pos = (wave * QLOADS + i) * 64 + lane;
       const int row = pos / CPR, phys = pos % CPR;
-      qdma[i] = (uint32_t)(row * qs * 2 + ((phys ^ swz_k<D>(row)) << 4));
+      // (q0 is a multiple of grp, so block row `row` is row_off(row) past row q0)
+      qdma[i] = (uint32_t)(row_off(row) * 2 + ((phys ^ swz_k<D>(row)) << 4));
     }
-    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
-    copy_rows_to_lds<QLOADS>((const void*)(Qp + (long long)q0 * qs), bytes, qsm + wave * QLOADS * 1024, qdma);
+    // bytes from row q0 to the end of the last valid row
+    const uint32_t bytes = PACK ? (uint32_t)((q_len - q0 / grp - 1) * qs + grp * D) * 2u
+                                : (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
+    copy_rows_to_lds<QLOADS>((const void*)(Qp + row_off(q0)), bytes, qsm + wave * QLOADS * 1024, qdma);
   }
 
   // per-lane LDS byte offsets, invariant over tiles
@@ -250,6 +270,7 @@ fwd_kernel(FwdParams p) {
   float l_run = 0.f;
   const float c = p.scale_log2;
   const int qi = qw + qlane;
+  const int qpos = row_pos(qi);   // causal position of the lane's query
   const char* const qwave = qsm + wave * 32 * ROW;   // this wave's Q rows (QLDS)
 
   auto read_v = [&](i16x4 (&vr)[2 * DB], uint32_t vstage, auto cc_tag) {
@@ -296,7 +317,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * bb + 16 * (i >> 3) + 8 * h + (i & 7);
-          const bool dead = (key >= kv_len) || (CAUSAL && key > qi - key0);
+          const bool dead = (key >= kv_len) || (CAUSAL && key > qpos - key0);
           sn[bb][i] = dead ? NEG_INF : sn[bb][i];
         }
     }
@@ -445,7 +466,7 @@ fwd_kernel(FwdParams p) {
 
   // tiles this wave computes (a causal wave stops at its diagonal; a wave
   // whose rows see no key still runs one fully masked tile)
-  const int n_w = CAUSAL ? min(ntile, max(cw + 31, 0) / BN + 1) : ntile;
+  const int n_w = CAUSAL ? min(ntile, max(cw_hi, 0) / BN + 1) : ntile;
 
   // Round r (r = 0 .. ntile) precedes tile r-1's work (and the first tile's
   // S).  Two stages: wait for all copies, barrier, start K_{r+1} and V_r into
@@ -509,11 +530,11 @@ fwd_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + wave_half_swap(l_run);
-  if (SPLIT && qi < q_len) {
+  if (SPLIT && qi < rows_len) {
     // fp32 partial of this key range: O_p = sum P V / l_p, LSE_p
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const long long plane = (long long)split * p.B * p.Sq * p.Hq;
-    float* orow = p.o_part + (plane * D + q_off + (long long)qi * qs + hq * D);
+    float* orow = p.o_part + (plane * D + q_off + hq * D + row_off(qi));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -527,11 +548,11 @@ fwd_kernel(FwdParams p) {
       }
     if (h == 0) {
       const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
-      p.lse_part[plane + lse_off + qi] = lse;
+      p.lse_part[plane + lse_idx(qi)] = lse;
     }
-  } else if (qi < q_len) {
+  } else if (qi < rows_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T* orow = Op + (long long)qi * qs;
+    T* orow = Op + row_off(qi);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -544,7 +565,7 @@ fwd_kernel(FwdParams p) {
       }
     if (p.lse != nullptr && h == 0) {
       const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
-      p.lse[lse_off + qi] = lse;
+      p.lse[lse_idx(qi)] = lse;
     }
   }
 }
@@ -556,25 +577,35 @@ constexpr int fwd_lds_bytes() {
   return 2 * (NW == 8 ? 3 : 2) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
 }
 
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false>
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false, bool PACK = false>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   constexpr int lds = fwd_lds_bytes<D, BN, NW>();
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  auto* kern = fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT, PACK>;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT>), dim3(p.grid), dim3(64 * NW), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
-// Split-KV partials: 4-wave (128-row) blocks, dense inputs
-template <typename T, int D>
-static hipError_t launch_split_t(const FwdParams& p, int causal, hipStream_t s) {
-  return causal ? launch_one<T, D, 64, 4, true, false, true>(p, s) : launch_one<T, D, 64, 4, false, false, true>(p, s);
+// Dense 4-wave (128-row) blocks, optionally split-KV and / or PackGQA
+template <typename T, int D, bool SPLIT>
+static hipError_t launch_dense4(const FwdParams& p, int causal, hipStream_t s) {
+  if (p.pack)
+    return causal ? launch_one<T, D, 64, 4, true, false, SPLIT, true>(p, s)
+                  : launch_one<T, D, 64, 4, false, false, SPLIT, true>(p, s);
+  return causal ? launch_one<T, D, 64, 4, true, false, SPLIT, false>(p, s)
+                : launch_one<T, D, 64, 4, false, false, SPLIT, false>(p, s);
+}
+
+template <bool SPLIT>
+static hipError_t launch_dense4_any(const FwdParams& p, int dtype, int d, int causal, hipStream_t s) {
+  if (dtype == 0)
+    return d == 128 ? launch_dense4<__bf16, 128, SPLIT>(p, causal, s) : launch_dense4<__bf16, 64, SPLIT>(p, causal, s);
+  return d == 128 ? launch_dense4<_Float16, 128, SPLIT>(p, causal, s) : launch_dense4<_Float16, 64, SPLIT>(p, causal, s);
 }
 
 hipError_t launch_fwd_split(const FwdParams& p, int dtype, int d, int causal, hipStream_t s) {
-  if (dtype == 0) return d == 128 ? launch_split_t<__bf16, 128>(p, causal, s) : launch_split_t<__bf16, 64>(p, causal, s);
-  return d == 128 ? launch_split_t<_Float16, 128>(p, causal, s) : launch_split_t<_Float16, 64>(p, causal, s);
+  return launch_dense4_any<true>(p, dtype, d, causal, s);
 }
 
 template <typename T, int D, int BN, int NW>
@@ -613,6 +644,7 @@ static bool use_wide() {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (p.pack && !varlen) return launch_dense4_any<false>(p, dtype, d, causal, s);
   const int bm = fwd_block_m(dtype, d, varlen);
   if (bm == 256 && d == 128 && !varlen && use_wide()) return launch_fwd_wide(p, dtype, causal, s);
   if (bm == 256) {

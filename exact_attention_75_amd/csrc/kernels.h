@@ -32,7 +32,12 @@ struct FwdParams {
   int split_keys = 0;
   float* o_part = nullptr;    // [splits, B, Sq, Hq, D] fp32
   float* lse_part = nullptr;  // [splits, B, Hq, Sq] fp32
+  // PackGQA (dense, 128-row blocks): tm runs over (B, Hkv, Sq * group) and a
+  // tile's rows are (position, head of the group) pairs
+  int pack = 0;
 };
+
+constexpr int kCombineMaxSplits = 256;   // most partials attn_combine merges per row
 
 struct CombineParams {
   const float* o_part;        // [splits, B, Sq, Hq, d]
@@ -72,12 +77,13 @@ int fwd_block_m(int dtype, int d, int varlen);
 // Query rows per workgroup of the fp8 forward.
 int fwd_fp8_block_m();
 
-// Returns hipSuccess or the launch error.
+// Returns hipSuccess or the launch error.  p.pack selects the PackGQA
+// variant (128-row blocks) for dense inputs.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
 // d = 128 dense bf16/fp16 with 256-row blocks, one wave per SIMD.
 hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s);
-// Split-KV partials with the 4-wave kernel (dense, d in {64, 128}); grid =
-// splits x tiles, split index slowest.
+// Split-KV partials with the 4-wave kernel (dense, d in {64, 128}, optionally
+// PackGQA); grid = splits x tiles, split index slowest.
 hipError_t launch_fwd_split(const FwdParams& p, int dtype, int d, int causal, hipStream_t s);
 // Merge of split-KV partials into O (dtype 0 bf16, 1 fp16) and LSE.
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);

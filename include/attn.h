@@ -88,6 +88,8 @@ enum attn_status {
  * scale: multiplies Q K^T before the softmax; must be finite and > 0
  *   (1/sqrt(d) gives the formula's 1/sqrt(d_k)).
  * causal: non-zero hides key j from query i when j > i.
+ * bf16/fp16 dense calls with GQA and few query positions use PackGQA (see
+ *   attn_fwd_splitkv); the result does not depend on that choice.
  * dtype: an attn_dtype.  For the fp8 types q, k, v are fp32 and o is bf16;
  *   the quantised copies live in a library-owned, lazily grown device
  *   workspace (released by attn_release); the Hadamard variant uses the
@@ -153,8 +155,16 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
  * cu_seqlens); dtype ATTN_BF16 or ATTN_FP16.
  * num_splits: the number of key ranges wanted (0 = chosen by the library,
  *   see attn_split_plan; at most 256).  The plan rounds range lengths up to
- *   multiples of 64 keys, so fewer ranges may result; with one range the
- *   call is attn_fwd.
+ *   multiples of 64 keys, so fewer ranges may result; with one range no
+ *   partials are written and the kernels of attn_fwd run.
+ * pack_gqa: PackGQA ("FlashAttention-3 Deep Dive" API surface, the
+ *   pack_gqa option; Hopper tag page, contents 11): the query rows of all
+ *   Hq / Hkv heads that share a KV head go into one 128-row tile, row
+ *   position * (Hq / Hkv) + head-in-group, so that few query positions still
+ *   fill a tile and each K/V tile is read once per group.  -1 = automatic
+ *   (packed when that gives fewer tiles, e.g. decoding), 0 = off, 1 = on
+ *   (needs Hq / Hkv to divide 128, else ATTN_ERR_ARG; a no-op without GQA).
+ *   attn_fwd makes the automatic choice.
  * The partials live in a library-owned, lazily grown device workspace
  * (splits * B * Sq * Hq * (d + 1) floats; released by attn_release).  Calls
  * on different streams of one device share it and must not overlap.
@@ -162,18 +172,23 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
  */
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
-                     int num_splits, int dtype, void* stream);
+                     int num_splits, int pack_gqa, int dtype, void* stream);
 
 /*
- * attn_split_plan -- the key ranges attn_fwd_splitkv uses: writes the number
- * of ranges and the keys per range (a multiple of 64; the last range holds
- * the rest, no range is empty).  num_splits == 0 picks enough ranges for
- * about 1024 workgroups of 128 query rows, each range >= 256 keys, at most
- * 64 ranges.  Returns ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_ARG
- * (num_splits < 0 or > 256) or ATTN_ERR_SIZE.
+ * attn_split_plan -- the plan attn_fwd_splitkv follows for these arguments:
+ * writes the number of key ranges, the keys per range (a multiple of 64; the
+ * last range holds the rest, no range is empty) and whether the tiles are
+ * packed (PackGQA, 0 or 1).  num_splits == 0 weighs the rounds of
+ * workgroups the device runs (256 CUs; one 128-row workgroup per CU with
+ * d = 128, two with d = 64) against the keys each workgroup covers plus a
+ * fixed cost per workgroup worth 128 keys, and takes the cheapest count
+ * (ranges of >= 256 keys, at most 64).  Returns ATTN_OK, ATTN_ERR_NULL,
+ * ATTN_ERR_SHAPE, ATTN_ERR_GQA, ATTN_ERR_HEADDIM, ATTN_ERR_ARG (num_splits
+ * < 0 or > 256; pack_gqa not in {-1, 0, 1}, or 1 with a group size that
+ * does not divide 128) or ATTN_ERR_SIZE.
  */
-int attn_split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits_out,
-                    int* split_keys_out);
+int attn_split_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits, int pack_gqa,
+                    int* splits_out, int* split_keys_out, int* pack_out);
 
 /*
  * attn_combine -- merge of split-KV partials (the Hopper tag page,
@@ -187,7 +202,9 @@ int attn_split_plan(int B, int Hq, int Sq, int Sk, int num_splits, int* splits_o
  *   o        [B, Sq, Hq, d] in dtype (ATTN_BF16 / ATTN_FP16), rounded to
  *            nearest even,
  *   lse      [B, Hq, Sq] fp32, may be NULL.
- * All device pointers, caller-owned.  d must be 64 or 128.
+ * All device pointers, caller-owned.  d must be 64 or 128; 1 <= splits <= 256
+ * (more gives ATTN_ERR_ARG).  The O_p of a partial whose LSE_p is -inf is
+ * never used and may hold anything.
  */
 int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse, int splits,
                  int B, int Hq, int Sq, int d, int dtype, void* stream);

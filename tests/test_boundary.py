@@ -112,12 +112,12 @@ def test_tile_of_rejects_bad_args(lib):
         ea.tile_of(0, 1, 3, 2, 256, 128, False)
 
 
-@pytest.mark.parametrize("B,Hq,Sq,Sk,n", [
-    (4, 32, 1, 16384, 0), (1, 1, 1, 100, 0), (2, 8, 300, 5000, 0), (1, 2, 256, 1000, 3),
-    (1, 2, 256, 100, 7), (1, 2, 256, 129, 3), (1, 1, 1, 64, 256), (16, 64, 4096, 4096, 0),
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,n", [
+    (4, 32, 8, 1, 16384, 0), (1, 1, 1, 1, 100, 0), (2, 8, 8, 300, 5000, 0), (1, 2, 1, 256, 1000, 3),
+    (1, 2, 2, 256, 100, 7), (1, 2, 2, 256, 129, 3), (1, 1, 1, 1, 64, 256), (16, 64, 8, 4096, 4096, 0),
 ])
-def test_split_plan_covers_keys(lib, B, Hq, Sq, Sk, n):
-    splits, keys = ea.split_plan(B, Hq, Sq, Sk, n)
+def test_split_plan_covers_keys(lib, B, Hq, Hkv, Sq, Sk, n):
+    splits, keys, packed = ea.split_plan(B, Hq, Hkv, Sq, Sk, num_splits=n)
     assert keys % 64 == 0 and keys > 0
     # every range non-empty, together exactly [0, Sk)
     assert (splits - 1) * keys < Sk <= splits * keys
@@ -125,27 +125,35 @@ def test_split_plan_covers_keys(lib, B, Hq, Sq, Sk, n):
         assert splits <= n
     else:
         assert 1 <= splits <= 64
-        tiles = B * Hq * ((Sq + 127) // 128)
         if splits > 1:
-            assert keys >= 256 or Sk < 512
-            assert tiles * (splits - 1) < 1024
+            assert keys >= 256
 
 
 def test_split_plan_auto_decode_shape(lib):
-    # 128 tiles of one query row each -> 8 ranges of 2048 keys
-    assert ea.split_plan(4, 32, 1, 16384, 0) == (8, 2048)
-    # enough tiles already -> one range
-    assert ea.split_plan(2, 32, 8192, 8192, 0)[0] == 1
+    # decode, GQA 4:1: packed into 32 tiles of 4 rows -> 8 ranges of 2048
+    # keys fill the 256 CUs once
+    assert ea.split_plan(4, 32, 8, 1, 16384) == (8, 2048, True)
+    # unpacked: 128 tiles of one row -> 2 ranges (a third would need a
+    # second round of workgroups)
+    assert ea.split_plan(4, 32, 8, 1, 16384, pack_gqa=False) == (2, 8192, False)
+    # two workgroups per CU with d = 64
+    assert ea.split_plan(4, 32, 8, 1, 16384, d=64) == (16, 1024, True)
+    # enough tiles already -> one range, no packing
+    assert ea.split_plan(2, 32, 8, 8192, 8192) == (1, 8192, False)
+    # packing only where it gives fewer tiles
+    assert ea.split_plan(1, 8, 2, 100, 1000, num_splits=1)[2] is False     # ceil(200/128)=2 == 2*1
+    assert ea.split_plan(1, 8, 2, 64, 1000, num_splits=1)[2] is True       # 1 < 2
+    assert ea.split_plan(1, 8, 8, 1, 1000, num_splits=1, pack_gqa=True)[2] is False   # no groups to pack
 
 
 def test_splitkv_and_combine_validate(lib):
     def sk(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=64, Sk=256, d=64,
-                 scale=0.125, causal=0, n=2, dtype=0)
+                 scale=0.125, causal=0, n=2, pack=-1, dtype=0)
         a.update(kw)
         return lib.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
-                                    a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["n"], a["dtype"],
-                                    None)
+                                    a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["n"], a["pack"],
+                                    a["dtype"], None)
     assert sk(k=None) == -1
     assert sk(Sk=0) == -2
     assert sk(d=96) == -3
@@ -153,11 +161,14 @@ def test_splitkv_and_combine_validate(lib):
     assert sk(dtype=2) == -5 and sk(dtype=3) == -5
     assert sk(scale=float("nan")) == -6
     assert sk(n=-1) == -6 and sk(n=257) == -6
+    assert sk(pack=2) == -6 and sk(pack=-2) == -6
+    assert sk(Hq=6, Hkv=2, pack=1) == -6       # group 3 does not divide 128
     c = lambda **kw: lib.attn_combine(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("o", FAKE), None,
                                       kw.get("P", 2), kw.get("B", 1), 2, kw.get("Sq", 8), kw.get("d", 64),
                                       kw.get("dtype", 0), None)
     assert c(op=None) == -1 and c(o=None) == -1
     assert c(P=0) == -2 and c(Sq=0) == -2
+    assert c(P=257) == -6
     assert c(d=32) == -3
     assert c(dtype=2) == -5
-    assert lib.attn_split_plan(1, 1, 1, 1, 0, None, None) == -1
+    assert lib.attn_split_plan(1, 1, 1, 1, 1, 64, 0, -1, None, None, None) == -1

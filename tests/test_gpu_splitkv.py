@@ -1,4 +1,4 @@
-"""GPU parity of split-KV (flash-decoding) and the combine kernel, through the
+"""GPU parity of split-KV (flash-decoding), the combine kernel and PackGQA, through the
 C ABI, against the fp64 oracle on the same seeded inputs.
 
 attn_fwd_splitkv must give the attention over all keys (the oracle's
@@ -50,8 +50,9 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, tag):
     assert lmax <= LSE_ABS, (tag, lmax)
 
 
-def splitkv(ea, q, k, v, causal, n, scale=None):
-    o, lse = ea.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=n, scale=scale)
+def splitkv(ea, q, k, v, causal, n, scale=None, pack=None):
+    o, lse = ea.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=n, scale=scale,
+                            pack_gqa=pack)
     torch.cuda.synchronize()
     return o, lse
 
@@ -60,16 +61,66 @@ def splitkv(ea, q, k, v, causal, n, scale=None):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [2, 3, 7, 0])
+@pytest.mark.parametrize("pack", [None, False])
 @pytest.mark.parametrize("shape", [(2, 1, 1000, 8, 2), (1, 3, 777, 4, 4), (1, 130, 4100, 4, 1)])
-def test_splitkv_small_full(ea, dtype, d, causal, n, shape):
+def test_splitkv_small_full(ea, dtype, d, causal, n, pack, shape):
     B, Sq, Sk, Hq, Hkv = shape
-    splits, keys = ea.split_plan(B, Hq, Sq, Sk, n)
-    print(f"[case] splitkv dtype={dtype} d={d} causal={causal} n={n} shape={shape} plan={splits}x{keys}",
+    plan = ea.split_plan(B, Hq, Hkv, Sq, Sk, d=d, num_splits=n, pack_gqa=pack)
+    print(f"[case] splitkv dtype={dtype} d={d} causal={causal} n={n} pack={pack} shape={shape} plan={plan}",
           flush=True)
     q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, dtype, seed=(Sq * 31 + Sk + d) % 10000)
-    o, lse = splitkv(ea, q, k, v, causal, n)
+    o, lse = splitkv(ea, q, k, v, causal, n, pack=pack)
     o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
-    compare(o, lse, o_ref, l_ref, f"splitkv {dtype} d{d} c{int(causal)} n{n} {shape}")
+    compare(o, lse, o_ref, l_ref, f"splitkv {dtype} d{d} c{int(causal)} n{n} pack{pack} {shape}")
+
+
+# ---------------------------------------------------------------- PackGQA
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 1, 1000, 8, 2), (1, 3, 777, 8, 1), (1, 30, 500, 16, 4),
+                                   (3, 5, 130, 32, 2), (1, 1, 300, 128, 1)])
+def test_packgqa_plain_forward(ea, dtype, d, causal, shape):
+    # few query positions with GQA: attn_fwd packs the group's heads into one
+    # tile on its own (checked with the plan)
+    B, Sq, Sk, Hq, Hkv = shape
+    assert ea.split_plan(B, Hq, Hkv, Sq, Sk, d=d, num_splits=1)[2], shape
+    print(f"[case] packgqa fwd dtype={dtype} d={d} causal={causal} shape={shape}", flush=True)
+    q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, dtype, seed=(Sq * 7 + Sk + Hq) % 10000)
+    o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
+    compare(o, lse, o_ref, l_ref, f"packgqa fwd {dtype} d{d} c{int(causal)} {shape}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 4])
+@pytest.mark.parametrize("shape", [(1, 300, 300, 8, 2), (2, 257, 600, 16, 2), (1, 1000, 1000, 4, 1)])
+def test_packgqa_forced_many_tiles(ea, d, causal, n, shape):
+    # packing forced on shapes with many packed tiles: causal masks across
+    # tiles whose rows mix positions and heads, ragged last tile, with and
+    # without split-KV
+    B, Sq, Sk, Hq, Hkv = shape
+    plan = ea.split_plan(B, Hq, Hkv, Sq, Sk, d=d, num_splits=n, pack_gqa=True)
+    assert plan[2]
+    print(f"[case] packgqa forced d={d} causal={causal} n={n} shape={shape} plan={plan}", flush=True)
+    q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, "bf16", seed=(Sq + Sk + d + n) % 10000)
+    o, lse = splitkv(ea, q, k, v, causal, n, pack=True)
+    o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
+    compare(o, lse, o_ref, l_ref, f"packgqa forced d{d} c{int(causal)} n{n} {shape}")
+
+
+def test_packgqa_identical_v_rows_exact(ea):
+    # identical V rows in every KV head: O = v of the query's KV head exactly,
+    # with the group's heads packed into one tile
+    q, k, v = W.make_dense(2, 2, 700, 16, 2, 128, "bf16", seed=21)
+    v = v[:, :1].expand(2, 700, 2, 128).contiguous()
+    for causal in (False, True):
+        o, _ = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+        torch.cuda.synchronize()
+        want = v[:, :1].repeat_interleave(8, dim=2).expand(2, 2, 16, 128)
+        assert torch.equal(o.cpu(), want)
 
 
 @pytest.mark.parametrize("n", [2, 5, 16])
@@ -89,16 +140,18 @@ def test_splitkv_decode_shape(ea):
     B, Sq, Sk, Hq, Hkv, d = 4, 1, 16384, 32, 8, 128
     q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, "bf16", seed=12)
     for causal in (False, True):
-        print(f"[case] splitkv decode causal={causal} plan={ea.split_plan(B, Hq, Sq, Sk, 0)}", flush=True)
-        o, lse = splitkv(ea, q, k, v, causal, 0)
-        o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
-        compare(o, lse, o_ref, l_ref, f"splitkv decode c{int(causal)}")
+        for pack in (None, False):
+            print(f"[case] splitkv decode causal={causal} plan={ea.split_plan(B, Hq, Hkv, Sq, Sk, d=d, pack_gqa=pack)}",
+                  flush=True)
+            o, lse = splitkv(ea, q, k, v, causal, 0, pack=pack)
+            o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal)
+            compare(o, lse, o_ref, l_ref, f"splitkv decode c{int(causal)} pack{pack}")
 
 
 def test_splitkv_one_range_is_the_plain_forward(ea):
     q, k, v = W.make_dense(1, 300, 300, 2, 2, 64, "fp16", seed=13)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
-    o1, l1 = ea.fwd_splitkv(qc, kc, vc, causal=True, num_splits=1)
+    o1, l1 = ea.fwd_splitkv(qc, kc, vc, causal=True, num_splits=1, pack_gqa=False)
     o2, l2 = ea.fwd(qc, kc, vc, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
@@ -160,9 +213,19 @@ def test_combine_random_partials_with_empty_rows(ea):
     lp[:, 1, 2, 5] = -math.inf          # a row no partial saw
     lp[:, 0, 0, 7] = -math.inf
     lp[3, 0, 0, 7] = 12.5               # a row only one partial saw
+    op[torch.isneginf(lp).permute(0, 1, 3, 2)] = float("nan")   # partials with LSE -inf are never read
     o, lse = ea.combine(op.cuda(), lp.cuda(), dtype=torch.bfloat16)
     torch.cuda.synchronize()
     o_ref, l_ref = A.combine(op.double().numpy(), lp.double().numpy())
     compare(o, lse, o_ref, l_ref, "combine random")
+    # many partials (the most attn_combine takes), d = 64, fp16
+    P2 = 256
+    op2 = torch.randn(P2, 1, 5, 2, 64, generator=g) * 0.5
+    lp2 = torch.randn(P2, 1, 2, 5, generator=g) * 3.0
+    lp2[:200, 0, 1, 3] = -math.inf
+    o2, l2 = ea.combine(op2.cuda(), lp2.cuda(), dtype=torch.float16)
+    torch.cuda.synchronize()
+    o2_ref, l2_ref = A.combine(op2.double().numpy(), lp2.double().numpy())
+    compare(o2, l2, o2_ref, l2_ref, "combine 256 partials")
     assert torch.all(o[1, 5, 2] == 0) and math.isinf(lse[1, 2, 5].item())
     assert torch.equal(o[0, 7, 0].cpu(), op[3, 0, 7, 0].to(torch.bfloat16))

@@ -15,6 +15,9 @@ attention-forward scope names; the pages print no data of their own):
       fp16 causal within each sequence
   c5  B=1  H=16        S=16384  d=128  fp8 e4m3 (inputs fp32)  full; 4 of the 128
       channels scaled x20 in Q, K and V (outlier features), optional Hadamard
+  dec B=4  Hq=32 Hkv=8 Sq=1  Sk=16384  d=128  bf16  full  Q/K/V iid N(0,1): one
+      new token per sequence over a long key cache (c3's head layout), the
+      decode shape that split-KV serves
 
 Recipe: torch CPU generator, ``torch.randn`` in fp32, then a round-to-nearest-even
 cast to the kernel dtype.  Seeds: Q = 10*c, K = 10*c + 1, V = 10*c + 2 for
@@ -60,6 +63,8 @@ CONFIGS = {
                    varlen=True, seed_base=40),
     "c5": Workload("c5", B=1, Hq=16, Hkv=16, Sq=16384, Sk=16384, d=128, dtype="fp8", causal=False,
                    outliers=True, seed_base=50),
+    # decode: one query row per sequence against 16K keys
+    "dec": Workload("dec", B=4, Hq=32, Hkv=8, Sq=1, Sk=16384, d=128, dtype="bf16", causal=False, seed_base=60),
     # the 8K causal GQA shape run through the fp8 path (N(0,1) inputs, no outliers)
     "c3fp8": Workload("c3fp8", B=2, Hq=32, Hkv=8, Sq=8192, Sk=8192, d=128, dtype="fp8", causal=True,
                       seed_base=35),
