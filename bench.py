@@ -33,10 +33,13 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (bf16, fp8) and % of MFMA peak, 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 HBM_PEAK_GBS = 8000.0                                            # MI355X HBM3E
-_FWD_SOURCES = ("exact_attention_75_amd/csrc/attn_fwd.hip", "exact_attention_75_amd/csrc/attn_fwd_wide.hip",
-                "exact_attention_75_amd/csrc/wide_regs.h", "exact_attention_75_amd/csrc/kernel_common.h")
-KERNEL_SOURCES = {"bf16": _FWD_SOURCES, "fp16": _FWD_SOURCES,
-                  "fp8": ("exact_attention_75_amd/csrc/attn_fp8.hip", "exact_attention_75_amd/csrc/kernel_common.h")}
+# sources that define each measured kernel (its code and its tile order): the
+# committed HBM traffic of a kernel is used only while these are unchanged
+_CS = "exact_attention_75_amd/csrc/"
+_WIDE_SOURCES = (_CS + "attn_fwd_wide.hip", _CS + "wide_regs.h", _CS + "kernel_common.h", _CS + "tile_sched.h")
+KERNEL_SOURCES = {"bf16": _WIDE_SOURCES, "fp16": _WIDE_SOURCES,
+                  "fp8": (_CS + "attn_fp8.hip", _CS + "kernel_common.h", _CS + "tile_sched.h"),
+                  "splitkv": (_CS + "attn_fwd.hip", _CS + "kernel_common.h", _CS + "tile_sched.h")}
 
 
 def parse():
@@ -190,7 +193,8 @@ def splitkv_leg(ea, name, steps, warmup):
             "splits": splits, "split_keys": keys, "pack_gqa": packed,
             "step_ms": round(ms_s, 5), "plain_fwd_ms": round(ms_p, 5), "speedup_vs_plain": round(ms_p / ms_s, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+                         "traffic": traffic_for(w.name, "splitkv", 1)}}
 
 
 def time_steps(step, steps, warmup):
