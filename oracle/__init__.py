@@ -1,4 +1,4 @@
-"""Oracle for the fused exact-attention forward -- TEST INFRASTRUCTURE ONLY.
+"""Oracle for fused exact attention (forward and backward) -- TEST INFRASTRUCTURE ONLY.
 
 Plain, slow, fp64 CPU implementations of what the GPU path computes.  Nothing
 in the product (the ``exact_attention_75_amd`` package, its C-ABI library or its
@@ -10,7 +10,9 @@ Modules
   attention  the definition softmax(scale * Q K^T + mask) V with a per-row
              natural-log LSE, the full score matrix materialised per head;
              the same over a sub-range of the keys (the partial state of one
-             key split) and the combine formula that merges such partials
+             key split) and the combine formula that merges such partials;
+             the backward (dQ, dK, dV, with an optional LSE gradient) by the
+             chain rule through that definition
   fp8        OCP E4M3 encode/decode, per-128-row block quantisation, the
              Sylvester Hadamard matrix and the signed rotation
 

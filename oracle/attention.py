@@ -205,3 +205,92 @@ def attention_flops(Sq: int, Sk: int, d: int, causal: bool, B: int = 1, H: int =
     if lengths is not None:
         return 4.0 * d * H * sum(pairs(n, n) for n in lengths)
     return 4.0 * d * B * H * pairs(Sq, Sk)
+
+
+# ---------------------------------------------------------------- backward
+def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float, causal: bool,
+                  dlse: Optional[np.ndarray] = None, row_chunk: int = 1024):
+    """Gradients of one head's attention (fp64): q [Sq, d], k/v [Sk, d], the
+    output gradient do [Sq, d] and optionally the gradient of the LSE output
+    dlse [Sq]  ->  (dq [Sq, d], dk [Sk, d], dv [Sk, d]).
+
+    Chain rule through the definition (the backward gradient math listed in
+    the Hopper tag page, contents 7.1 -- 7.1.5; the section bodies are absent
+    from the pages, so this is the textbook derivation):
+      P = softmax(S), S = scale * q k^T (masked entries -inf, P = 0 there)
+      dV = P^T dO,  dP = dO V^T,
+      dS_ij = P_ij (dP_ij - D_i + dlse_i),  D_i = sum_j P_ij dP_ij = dO_i . O_i
+        (the softmax Jacobian; dLSE_i / dS_ij = P_ij adds the dlse term),
+      dQ = scale * dS K,  dK = scale * dS^T Q   (the scale is applied last).
+    Rows are independent in P and dS, so they may be taken in chunks; dK and
+    dV are sums over all rows.
+    """
+    Sq, d = q.shape
+    Sk = k.shape[0]
+    dq = np.zeros((Sq, d))
+    dk = np.zeros((Sk, k.shape[1]))
+    dv = np.zeros((Sk, v.shape[1]))
+    for c0 in range(0, Sq, row_chunk):
+        r = np.arange(c0, min(Sq, c0 + row_chunk))
+        p, _, _ = head_probs(q, k, scale, causal, r)      # [R, Sk], rows of P
+        o = p @ v
+        dor = do[r]
+        dv += p.T @ dor
+        dp = dor @ v.T
+        D = (dor * o).sum(axis=1)
+        if dlse is not None:
+            D = D - dlse[r]
+        ds = p * (dp - D[:, None])
+        dq[r] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r])
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool = False, dlse=None, cu_seqlens=None):
+    """Gradients of exact attention in fp64 (see ``head_backward``).
+
+    Dense:  q, do [B, Sq, Hq, d]; k, v [B, Sk, Hkv, d]; dlse [B, Hq, Sq] or None
+            -> dq [B, Sq, Hq, d], dk, dv [B, Sk, Hkv, d]
+    Varlen: q, do [T, Hq, d]; k, v [T, Hkv, d]; dlse [Hq, T] or None; cu_seqlens
+            -> dq [T, Hq, d], dk, dv [T, Hkv, d]
+    With GQA the gradient of a KV head is the sum over the query heads that
+    read it.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    dl = None if dlse is None else _as_f64(dlse)
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            if b <= a:
+                continue
+            g = attention_backward(q[None, a:b], k[None, a:b], v[None, a:b], do[None, a:b], scale, causal,
+                                   None if dl is None else dl[None, :, a:b])
+            dq[a:b], dk[a:b], dv[a:b] = g[0][0], g[1][0], g[2][0]
+        return dq, dk, dv
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            gq, gk, gv = head_backward(q[b, :, h], k[b, :, hk], v[b, :, hk], do[b, :, h], scale, causal,
+                                       None if dl is None else dl[b, h])
+            dq[b, :, h] = gq
+            dk[b, :, hk] += gk
+            dv[b, :, hk] += gv
+    return dq, dk, dv
+
+
+def attention_backward_flops(Sq: int, Sk: int, d: int, causal: bool, B: int = 1, H: int = 1) -> float:
+    """Algorithmic FLOP of the backward: five GEMMs of 2 d FLOP per unmasked
+    (query, key) pair each (recomputed S, dV, dP, dQ, dK) = 10 d per pair,
+    2.5 times the forward's 4 d."""
+    return 2.5 * attention_flops(Sq, Sk, d, causal, B=B, H=H)
