@@ -6,7 +6,7 @@ One step is one pass of the hot path over one batch of the workload: for the
 bf16/fp16 workloads one ``attn_fwd`` call; for the fp8 workloads the fp8
 prepass of Q, K and V plus the fp8 attention kernel; for the split-KV leg
 (decode shape) one ``attn_fwd_splitkv`` call, i.e. the split kernel and the
-combine kernel.  Inputs are resident in
+combine kernel; for the backward leg one ``attn_bwd`` call.  Inputs are resident in
 device memory before the timed region.  The timed region is bracketed by
 ``torch.cuda.synchronize()`` and measured with HIP events on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workloads")
     ap.add_argument("--no-split", action="store_true", help="skip the split-KV decode leg")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for the HBM byte counters)")
@@ -197,6 +198,40 @@ def splitkv_leg(ea, name, steps, warmup):
                          "traffic": traffic_for(w.name, "splitkv", 1)}}
 
 
+def bwd_leg(ea, name, steps, warmup):
+    """Backward on a bf16 workload: one step = one ``attn_bwd`` (statistics
+    preprocess + dK/dV kernel + dQ kernel), o and lse from the library's
+    forward.  Algorithmic FLOP: five GEMMs of 2 d per unmasked pair = 2.5x
+    the forward's."""
+    import torch
+    import workloads as W
+    from oracle.attention import attention_backward_flops  # counting rule only
+    w = W.CONFIGS[name]
+    _, dev = device_inputs(w)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed_base + 7)).to(q.dtype).cuda()
+    o, lse = ea.fwd(q, k, v, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    L = ea.library()
+    st = torch.cuda.current_stream().cuda_stream
+    dt = {"bf16": ea.ATTN_BF16, "fp16": ea.ATTN_FP16}[w.dtype]
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), None,
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, float(w.scale),
+            int(w.causal), dt, st)
+
+    def step():
+        rc = L.attn_bwd(*args)
+        if rc != 0:
+            raise RuntimeError(L.attn_strerror(rc).decode())
+    ms = time_steps(step, steps, warmup) / steps
+    fl = attention_backward_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.Sq} d={w.d} {w.dtype} "
+                        f"{'causal' if w.causal else 'full'} backward",
+            "step_ms": round(ms, 5), "tflops": round(tf, 2), "algorithmic_flop_per_step": fl,
+            "pct_of_dense_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 2)}
+
+
 def time_steps(step, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -314,6 +349,9 @@ def main():
                       "c5_hadamard": fp8_leg(ea, "c5", max(5, a.steps // 5), 3, hadamard=True)}
     if not a.no_split:
         out["splitkv"] = splitkv_leg(ea, "dec", max(20, a.steps), a.warmup)
+    if not a.no_bwd:
+        out["bwd"] = bwd_leg(ea, a.workload if W.CONFIGS[a.workload].dtype in ("bf16", "fp16")
+                             and not W.CONFIGS[a.workload].varlen else "c3", max(5, a.steps // 5), 3)
     if a.extra:
         for name in ("c1", "c2", "c4"):
             if name == a.workload:

@@ -10,6 +10,7 @@ or a call fails, an exception is raised.
     o, lse = fwd(q, k, v, causal=True)            # bf16 / fp16, dense or varlen
     o, lse = fwd(q32, k32, v32, dtype="fp8")      # fp32 inputs, fp8 GEMMs, bf16 out
     o, lse = fwd_splitkv(q, k, v, num_splits=0)   # key axis split over workgroups
+    dq, dk, dv = bwd(q, k, v, o, lse, do)         # gradients (bf16 / fp16, dense)
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
+__all__ = ["fwd", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
            "default_signs", "tile_of",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
@@ -66,6 +67,8 @@ def library() -> ctypes.CDLL:
     L.attn_split_plan.restype = I
     L.attn_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     L.attn_combine.restype = I
+    L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    L.attn_bwd.restype = I
     L.attn_strerror.argtypes = [I]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_release.argtypes = []
@@ -207,6 +210,31 @@ def combine(o_part: torch.Tensor, lse_part: torch.Tensor, dtype: torch.dtype = t
                                 _stream())
     _check(rc, "attn_combine")
     return o, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        do: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+        dlse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Attention backward through ``attn_bwd`` (dense bf16/fp16).
+
+    q, o, do [B, Sq, Hq, d]; k, v [B, Sk, Hkv, d]; lse (and the optional LSE
+    gradient dlse) fp32 [B, Hq, Sq] -> dq [B, Sq, Hq, d], dk, dv [B, Sk, Hkv, d]."""
+    _need_gpu(q, k, v, o, lse, do, dlse)
+    dt = _kernel_dtype(q, k, v, o, do)
+    if lse.dtype != torch.float32 or (dlse is not None and dlse.dtype != torch.float32):
+        raise ValueError("lse and dlse must be fp32")
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    rc = library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dlse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), dt,
+                            _stream())
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def fp8_prepass(x: torch.Tensor, transpose_out: bool = False,

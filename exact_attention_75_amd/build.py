@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 
@@ -111,7 +111,8 @@ def build(jobs: int = 4, save_temps: str | None = None) -> str:
     return LIB
 
 
-EXPECTED_KERNELS = ("fwd_kernel", "fwd_wide_kernel", "fwd_fp8_kernel", "prepass_kernel", "combine_kernel")
+EXPECTED_KERNELS = ("fwd_kernel", "fwd_wide_kernel", "fwd_fp8_kernel", "prepass_kernel", "combine_kernel",
+                    "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
 
 
 def check_kernels(path: str) -> None:

@@ -38,9 +38,10 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
 
 // --- workspaces: lazily grown device buffers, one per (use, device) -------
 // kWsFp8 holds the quantised operands of attn_fwd's fp8 types, kWsSplit the
-// split-KV partials; separate buffers, so the two paths never share memory.
+// split-KV partials, kWsBwd the backward's per-row statistics; separate
+// buffers, so the paths never share memory.
 constexpr int kMaxDevices = 64;
-enum { kWsFp8 = 0, kWsSplit = 1, kWsKinds = 2 };
+enum { kWsFp8 = 0, kWsSplit = 1, kWsBwd = 2, kWsKinds = 3 };
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -430,6 +431,47 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (rc) return rc;
   return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, splits, split_keys, dtype,
                      (hipStream_t)stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             const float* dlse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+             float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  const long long nkb = (Sk + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
+  if ((long long)B * Hkv * nkb > kMax32) return ATTN_ERR_SIZE;
+  const int sq_pad = (Sq + 31) / 32 * 32;
+  void* ws = nullptr;
+  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)B * Hq * sq_pad, &ws);
+  if (rc) return rc;
+  attn::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dlse = dlse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.stats = (float2*)ws;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Sq_pad = sq_pad;
+  p.group = Hq / Hkv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBwdBlockM, causal);
+  p.grid_dq = p.tm.ntiles;
+  p.grid_dkdv = (int)(B * Hkv * nkb);
+  hipError_t e = attn::launch_bwd(p, dtype, d, causal, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
 void attn_release(void) {

@@ -1,0 +1,469 @@
+// attn_bwd.hip -- attention backward for bf16 / fp16, d in {64, 128}, dense,
+// causal or not, GQA.
+//
+// Gradient math (the backward listed in the Hopper tag page, contents 7.1 --
+// 7.1.5; the chain rule through O = softmax(scale Q K^T + mask) V):
+//   P = exp(scale S - LSE) recomputed from the forward's LSE (no max pass),
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  delta_i = dO_i . O_i
+//   (minus dLSE_i when the LSE output has a gradient),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels:
+//   bwd_pre_kernel   per query row: (LSE log2 e, delta) into a small fp32
+//                    array [B, Hq, Sq_pad] (the preprocess of contents
+//                    7.3.1), padded to 32 rows per head.
+//   bwd_dkdv_kernel  one workgroup per (batch, KV head, 128 keys); each wave
+//                    owns 32 keys and keeps their K, V fragments and dK, dV
+//                    accumulators in registers, and walks the query blocks of
+//                    every query head of the KV group (so GQA sums in
+//                    registers and no atomics are needed).  Per 32-query step:
+//                    S = Q K^T and dP = dO V^T (query rows x keys, so the
+//                    accumulator of each is directly the B operand of the
+//                    next MFMAs), P, dS, then dV^T += dO^T P and
+//                    dK^T += Q^T dS with the transposed operands read from
+//                    LDS by ds_read_b64_tr_b16.
+//   bwd_dq_kernel    one workgroup per (batch, query head, 128 query rows),
+//                    like the forward: S^T = K Q^T, dP^T = V dO^T (a lane
+//                    owns a query, so LSE and delta are lane scalars),
+//                    dS^T, then dQ^T += K^T dS^T.
+// The pages resolve the dQ race across key blocks with atomics or
+// semaphores (contents 7.2.3, 7.6); here dQ has a kernel of its own, which
+// recomputes S and dP (7 GEMMs instead of 5) and is deterministic.
+//
+// Operand layouts follow the forward kernels: v_mfma_f32_32x32x16, lane l
+// supplies row l % 32 and 8 consecutive k values 8 (l / 32) .. + 7; the first
+// GEMM's rows are permuted (key_perm) so that its accumulator registers,
+// taken 8 at a time, are the next GEMM's B operand in natural order.
+// Tiles move global -> LDS with buffer_load ... lds; a tile read both ways is
+// stored twice, once with the row-read swizzle and once with the
+// transposed-read swizzle, so neither access has bank conflicts.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernel_common.h"
+#include "kernels.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------- preprocess
+// Rows i in [Sq, Sq_pad) of the statistics get (+inf, 0): P = 0 there.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
+  typedef typename Mma<T>::vec8 vec8;
+  const long long rows = (long long)p.B * p.Sq_pad * p.Hq;
+  const long long rp = (long long)blockIdx.x * 256 + threadIdx.x;  // (b * Sq_pad + i) * Hq + h
+  if (rp >= rows) return;
+  const int hq = (int)(rp % p.Hq);
+  const long long bi = rp / p.Hq;
+  const int i = (int)(bi % p.Sq_pad);
+  const int b = (int)(bi / p.Sq_pad);
+  const long long li = ((long long)b * p.Hq + hq) * p.Sq_pad + i;
+  if (i >= p.Sq) {
+    p.stats[li] = make_float2(__builtin_inff(), 0.f);
+    return;
+  }
+  const long long r = ((long long)b * p.Sq + i) * p.Hq + hq;        // token-major row of o, dO
+  const T* o = (const T*)p.o + r * D;
+  const T* g = (const T*)p.dout + r * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const vec8 x = *(const vec8*)(o + c);
+    const vec8 y = *(const vec8*)(g + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+  }
+  const long long lo = ((long long)b * p.Hq + hq) * p.Sq + i;       // index in lse, dlse
+  if (p.dlse != nullptr) acc -= p.dlse[lo];
+  const float l = p.lse[lo];
+  // a row that saw no key has LSE = -inf and P = 0: +inf makes exp2 give 0
+  const float l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * 1.4426950408889634f;
+  p.stats[li] = make_float2(l2, acc);
+}
+
+// Per-lane LDS byte offsets of the two read patterns over a tile of rows of
+// D 16-bit elements (row stride 2 D bytes):
+//   row reads  (A/B operand, 8 consecutive elements of row key_perm(l % 32)):
+//              koff(kk) = koff0 ^ (kk << 5), +32 rows per 32-row block;
+//   transposed (A operand: 32 columns x 16 rows, ds_read_b64_tr_b16 pairs):
+//              voff(db) = voff0 ^ (db << 6), + 16 rows per chunk, second
+//              read + 4 rows.
+template <int D>
+struct TileReads {
+  static constexpr int ROW = 2 * D;
+  int koff0;
+  uint32_t voff0;
+  __device__ __forceinline__ TileReads(int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    const int r0 = key_perm(l32);
+    koff0 = r0 * ROW + ((h ^ swz_k<D>(r0)) << 4);
+    const int G = lane >> 4, i16 = lane & 15;
+    const int r = 8 * h + (i16 >> 2);
+    const int dd = 16 * (G & 1) + 4 * (i16 & 3);
+    voff0 = r * ROW + (((dd >> 3) ^ swz_v<D>(r)) << 4) + ((dd & 7) << 1);
+  }
+  __device__ __forceinline__ int koff(int kk) const { return koff0 ^ (kk << 5); }
+  __device__ __forceinline__ uint32_t voff(int db) const { return voff0 ^ (uint32_t)(db << 6); }
+};
+
+// DMA offsets of the copy of a tile of ROWS rows (row stride `stride`
+// elements in global memory) by NW waves, for either swizzle.
+template <int D, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int LOADS = ROWS * CPR / (NW * 64);
+  static_assert(LOADS >= 1 && ROWS * CPR % (NW * 64) == 0, "tile copy shape");
+  uint32_t k[LOADS], v[LOADS];
+  __device__ __forceinline__ TileCopy(int wave, int lane, int stride) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int pos = (wave * LOADS + i) * 64 + lane;
+      const int row = pos / CPR, phys = pos % CPR;
+      k[i] = (uint32_t)(row * stride * 2 + ((phys ^ swz_k<D>(row)) << 4));
+      v[i] = (uint32_t)(row * stride * 2 + ((phys ^ swz_v<D>(row)) << 4));
+    }
+  }
+};
+
+// A operand (32 columns of block db x 16 rows of chunk cc) from a tile stored
+// with the transposed-read swizzle
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::vec8 read_tr(uint32_t base, const TileReads<D>& tr, int db, int cc) {
+  const uint32_t a = base + tr.voff(db) + cc * 16 * (2 * D);
+  const i16x4 lo = lds_tr16<0>(a);
+  const i16x4 hi = lds_tr16<4 * 2 * D>(a);
+  i16x4 r[2] = {lo, hi};
+  lds_wait<0>(r);
+  const i16x8 w = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(typename Mma<T>::vec8, w);
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
+  typedef typename Mma<T>::vec8 vec8;
+  constexpr int BMQ = 32;                 // query rows per step
+  constexpr int KT = D / 16;              // k-steps over the head dimension
+  constexpr int DB = D / 32;              // 32-column blocks of dK^T, dV^T
+  constexpr int ROW = 2 * D;
+  constexpr int QT = BMQ * ROW;           // one 32-row tile
+  constexpr int STAT = 1024;              // (lse2, delta) of 32 rows, in a 1 KiB slot
+  // stage: [Q row-swizzled | Q transposed-swizzled | dO row | dO transposed | stats]
+  constexpr int STAGE = 4 * QT + STAT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  // key blocks in ascending order first: with causal masking the first ones
+  // see the most queries (longest first)
+  const int G = p.B * p.Hkv;
+  const int nblk = blockIdx.x / G;
+  const int gi = blockIdx.x % G;
+  const int b = gi / p.Hkv, hkv = gi % p.Hkv;
+  const int k0 = nblk * kBwdBlockN;
+  const int key = k0 + wave * 32 + l32;   // this lane's key (column of S)
+  const int qs = p.Hq * D;                // token stride of q, o, dO, dQ
+
+  // K and V of the lane's key as B operands (k = head dimension); rows past
+  // the end read a valid row and are masked
+  vec8 kf[KT], vf[KT];
+  {
+    const long long row = ((long long)b * p.Sk + min(key, p.Sk - 1)) * p.Hkv + hkv;
+    const T* kr = (const T*)p.k + row * D + 8 * h;
+    const T* vr = (const T*)p.v + row * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      kf[kk] = *(const vec8*)(kr + 16 * kk);
+      vf[kk] = *(const vec8*)(vr + 16 * kk);
+    }
+  }
+  f32x16 dv[DB], dk[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dv[i] = f32x16{};
+    dk[i] = f32x16{};
+  }
+
+  const int nM = (p.Sq + BMQ - 1) / BMQ;
+  const int m_begin = CAUSAL ? min(k0 / BMQ, nM) : 0;   // queries before k0 see none of these keys
+  const int per_head = nM - m_begin;
+  const int nsteps = p.group * per_head;
+
+  const TileCopy<D, BMQ, 4> cp(wave, lane, qs);
+  const TileReads<D> rd(lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+
+  auto step_coords = [&](int s, int& hq, int& q0) {
+    const int hg = s / per_head;
+    hq = hkv * p.group + hg;
+    q0 = (m_begin + s % per_head) * BMQ;
+  };
+  auto issue = [&](int s) {
+    int hq, q0;
+    step_coords(s, hq, q0);
+    char* st = smem + (s & 1) * STAGE;
+    const long long off = ((long long)b * p.Sq + q0) * qs + hq * D;
+    const uint32_t bytes = (uint32_t)(p.Sq - q0) * (uint32_t)qs * 2u;
+    const T* qb = (const T*)p.q + off;
+    const T* gb = (const T*)p.dout + off;
+    constexpr int L = TileCopy<D, BMQ, 4>::LOADS;
+    copy_rows_to_lds<L>(qb, bytes, st + 0 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
+    copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
+    if (wave == 0) {
+      // 32 (lse2, delta) pairs = 16 lanes x 16 bytes (the array is padded to
+      // 32 rows per head, so no 16-byte read straddles its end); the other
+      // lanes' offsets are out of range and write zeros past the pairs
+      const float2* sb = p.stats + ((long long)b * p.Hq + hq) * p.Sq_pad + q0;
+      copy_row_to_lds(sb, (uint32_t)(p.Sq_pad - q0) * 8u, st + 4 * QT, lane < 16 ? (uint32_t)lane * 16u : 0x40000000u);
+    }
+  };
+
+  const float c = p.scale_log2;
+  if (nsteps > 0) issue(0);
+  for (int s = 0; s < nsteps; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 1 < nsteps) issue(s + 1);
+    int hq, q0;
+    step_coords(s, hq, q0);
+    (void)hq;
+    const char* st = smem + (s & 1) * STAGE;
+    const uint32_t stl = lds0 + (s & 1) * STAGE;
+
+    // S = Q K^T and dP = dO V^T: row m of the MFMA is query key_perm(m)
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      const vec8 qa = *(const vec8*)(st + 0 * QT + rd.koff(kk));
+      const vec8 ga = *(const vec8*)(st + 2 * QT + rd.koff(kk));
+      sacc = Mma<T>::run(qa, kf[kk], sacc);
+      pacc = Mma<T>::run(ga, vf[kk], pacc);
+    }
+    // register r = 4 g + i holds query 16 (g >> 1) + 8 h + 4 (g & 1) + i:
+    // 4 consecutive queries per g, read as 2 x 16 bytes of (lse2, delta)
+    const float* sp = (const float*)(st + 4 * QT);
+    vec8 pv[2], dsv[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qr = 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+      const float4 s01 = *(const float4*)(sp + 2 * qr);
+      const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
+      const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
+      const float dl[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const int qrow = q0 + qr + i;
+        const bool dead = (key >= p.Sk) || (CAUSAL && key > qrow);
+        const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2[i]));
+        const float ds = pr * (pacc[r] - dl[i]);
+        pv[g >> 1][4 * (g & 1) + i] = (T)pr;
+        dsv[g >> 1][4 * (g & 1) + i] = (T)ds;
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (k = 16 queries per step)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const vec8 ga = read_tr<T, D>(stl + 3 * QT, rd, db, cc);
+        dv[db] = Mma<T>::run(ga, pv[cc], dv[db]);
+        const vec8 qa = read_tr<T, D>(stl + 1 * QT, rd, db, cc);
+        dk[db] = Mma<T>::run(qa, dsv[cc], dk[db]);
+      }
+  }
+
+  // dK^T, dV^T: lane holds key `key` and channels 32 db + 8 g + 4 h + 0..3
+  if (key < p.Sk) {
+    const long long row = ((long long)b * p.Sk + key) * p.Hkv + hkv;
+    T* dkr = (T*)p.dk + row * D;
+    T* dvr = (T*)p.dv + row * D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (T)(dk[db][4 * g + e] * p.scale);
+          wv[e] = (T)dv[db][4 * g + e];
+        }
+        *(T4*)(dkr + 32 * db + 8 * g + 4 * h) = wk;
+        *(T4*)(dvr + 32 * db + 8 * g + 4 * h) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
+  typedef typename Mma<T>::vec8 vec8;
+  constexpr int BN = 64;                  // keys per tile
+  constexpr int NB = BN / 32;
+  constexpr int KT = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int ROW = 2 * D;
+  constexpr int TILE = BN * ROW;
+  // stage: [K row-swizzled | K transposed-swizzled | V row-swizzled]
+  constexpr int STAGE = 3 * TILE;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, mblk;
+  tile_decode(p.tm, (int)blockIdx.x, b, hq, mblk);
+  const int hkv = hq / p.group;
+  const int qs = p.Hq * D;
+  const int ks = p.Hkv * D;
+  const int q0 = mblk * kBwdBlockM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + key_perm(l32);      // this lane's query (column of S^T)
+  const int qc = min(qi, p.Sq - 1);       // rows past the end compute on a valid row, never stored
+  const int q_hi = min(q0 + kBwdBlockM, p.Sq);
+  const int kv_end = CAUSAL ? min(p.Sk, q_hi) : p.Sk;
+  const int ntile = (kv_end + BN - 1) / BN;
+
+  // Q and dO of the lane's query as B operands (k = head dimension)
+  vec8 qf[KT], gf[KT];
+  {
+    const long long row = ((long long)b * p.Sq + qc) * p.Hq + hq;
+    const T* qr = (const T*)p.q + row * D + 8 * h;
+    const T* gr = (const T*)p.dout + row * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      qf[kk] = *(const vec8*)(qr + 16 * kk);
+      gf[kk] = *(const vec8*)(gr + 16 * kk);
+    }
+  }
+  const float2 st2 = p.stats[((long long)b * p.Hq + hq) * p.Sq_pad + qc];
+  const float l2 = st2.x, dl = st2.y;
+  const float c = p.scale_log2;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  const TileCopy<D, BN, 4> cp(wave, lane, ks);
+  const TileReads<D> rd(lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+  const T* kbase = (const T*)p.k + (long long)b * p.Sk * ks + hkv * D;
+  const T* vbase = (const T*)p.v + (long long)b * p.Sk * ks + hkv * D;
+  auto issue = [&](int t) {
+    char* st = smem + (t & 1) * STAGE;
+    const int j0 = t * BN;
+    const uint32_t bytes = (uint32_t)(p.Sk - j0) * (uint32_t)ks * 2u;
+    constexpr int L = TileCopy<D, BN, 4>::LOADS;
+    copy_rows_to_lds<L>(kbase + (long long)j0 * ks, bytes, st + 0 * TILE + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(kbase + (long long)j0 * ks, bytes, st + 1 * TILE + wave * L * 1024, cp.v);
+    copy_rows_to_lds<L>(vbase + (long long)j0 * ks, bytes, st + 2 * TILE + wave * L * 1024, cp.k);
+  };
+  // tiles this wave needs (a causal wave stops at its diagonal); every wave
+  // still takes part in every round's barrier
+  const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
+
+  if (ntile > 0) issue(0);
+  for (int t = 0; t < ntile; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < ntile) issue(t + 1);
+    if (t >= n_w) continue;
+    const char* st = smem + (t & 1) * STAGE;
+    const uint32_t stl = lds0 + (t & 1) * STAGE;
+    const int j0 = t * BN;
+
+    // S^T = K Q^T, dP^T = V dO^T: row m of block bb is key j0 + 32 bb + key_perm(m)
+    f32x16 sacc[NB], pacc[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      sacc[bb] = f32x16{};
+      pacc[bb] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const vec8 ka = *(const vec8*)(st + 0 * TILE + rd.koff(kk) + bb * 32 * ROW);
+        const vec8 va = *(const vec8*)(st + 2 * TILE + rd.koff(kk) + bb * 32 * ROW);
+        sacc[bb] = Mma<T>::run(ka, qf[kk], sacc[bb]);
+        pacc[bb] = Mma<T>::run(va, gf[kk], pacc[bb]);
+      }
+    // dS^T; chunk cc (16 keys) = registers 8 (cc & 1) .. + 7 of block cc >> 1
+    vec8 dsv[2 * NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = r >> 2, i = r & 3;
+        const int key = j0 + 32 * bb + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i;
+        const bool dead = (key >= p.Sk) || (CAUSAL && key > qi);
+        const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c, -l2));
+        dsv[2 * bb + (r >> 3)][r & 7] = (T)(pr * (pacc[bb][r] - dl));
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2 * NB; ++cc) {
+        const vec8 ka = read_tr<T, D>(stl + 1 * TILE, rd, db, cc);
+        dq[db] = Mma<T>::run(ka, dsv[cc], dq[db]);
+      }
+  }
+
+  if (qi < p.Sq) {
+    T* dqr = (T*)p.dq + ((long long)b * p.Sq + qi) * qs + hq * D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (T)(dq[db][4 * g + e] * p.scale);
+        *(T4*)(dqr + 32 * db + 8 * g + 4 * h) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+  const long long rows = (long long)p.B * p.Sq_pad * p.Hq;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int lds_kv = 2 * (4 * 32 * 2 * D + 1024);
+  constexpr int lds_q = 2 * (3 * 64 * 2 * D);
+  static const hipError_t a1 =
+      hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+  static const hipError_t a2 =
+      hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(p.grid_dkdv), dim3(256), lds_kv, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(p.grid_dq), dim3(256), lds_q, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_d(const BwdParams& p, int d, int causal, hipStream_t s) {
+  if (d == 128) return causal ? launch_bwd_t<T, 128, true>(p, s) : launch_bwd_t<T, 128, false>(p, s);
+  return causal ? launch_bwd_t<T, 64, true>(p, s) : launch_bwd_t<T, 64, false>(p, s);
+}
+
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, hipStream_t s) {
+  return dtype == 0 ? launch_bwd_d<__bf16>(p, d, causal, s) : launch_bwd_d<_Float16>(p, d, causal, s);
+}
+
+}  // namespace attn

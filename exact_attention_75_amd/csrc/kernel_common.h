@@ -99,9 +99,11 @@ __device__ __forceinline__ void lds_wait(i16x4 (&r)[N]) {
                  : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
                    "+v"(r[7])
                  : "n"(LEFT));
-  } else {
-    static_assert(N == 4, "");
+  } else if constexpr (N == 4) {
     asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(LEFT));
+  } else {
+    static_assert(N == 2, "");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(LEFT));
   }
 }
 

@@ -47,6 +47,28 @@ struct CombineParams {
   int splits, B, Hq, Sq, d;
 };
 
+struct BwdParams {
+  const void* q;              // [B, Sq, Hq, D]
+  const void* k;              // [B, Sk, Hkv, D]
+  const void* v;              // [B, Sk, Hkv, D]
+  const void* o;              // [B, Sq, Hq, D] forward output
+  const void* dout;           // [B, Sq, Hq, D] gradient of o
+  const float* lse;           // [B, Hq, Sq] forward LSE (natural log)
+  const float* dlse;          // [B, Hq, Sq] gradient of lse, or nullptr
+  void* dq;                   // [B, Sq, Hq, D]
+  void* dk;                   // [B, Sk, Hkv, D]
+  void* dv;                   // [B, Sk, Hkv, D]
+  float2* stats;              // [B, Hq, Sq_pad]: (LSE * log2 e, or +inf for -inf; delta)
+  int B, Hq, Hkv, Sq, Sk;
+  int Sq_pad;                 // Sq rounded up to 32 (rows past Sq: (+inf, 0))
+  int group;
+  float scale;
+  float scale_log2;           // scale * log2(e)
+  TileMap tm;                 // dQ tiles (128 query rows)
+  int grid_dq;
+  int grid_dkdv;
+};
+
 struct Fp8FwdParams {
   const uint8_t* q8;          // [B, Sq, Hq, 128]
   const uint8_t* k8;          // [B, Sk, Hkv, 128]
@@ -88,6 +110,11 @@ hipError_t launch_fwd_split(const FwdParams& p, int dtype, int d, int causal, hi
 // Merge of split-KV partials into O (dtype 0 bf16, 1 fp16) and LSE.
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s);
+// Backward: statistics preprocess, dK/dV (parallel over key blocks), dQ
+// (parallel over query blocks); dense bf16/fp16, d in {64, 128}.
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, hipStream_t s);
+constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
+constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);
 
 }  // namespace attn

@@ -209,6 +209,31 @@ int attn_split_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_split
 int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse, int splits,
                  int B, int Hq, int Sq, int d, int dtype, void* stream);
 
+/*
+ * attn_bwd -- attention backward (bf16 / fp16, dense, d = 64 or 128).
+ *
+ * Gradients of O = softmax(scale Q K^T + mask) V (and of LSE when dlse is
+ * given), by the chain rule listed in the Hopper tag page (l1-ca0.github.io,
+ * contents 7.1): P is recomputed from the forward's LSE,
+ *   dV = P^T dO,  dP = dO V^T,  delta_i = dO_i . O_i - dlse_i,
+ *   dS = P (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK, dV of a KV head summed over the Hq / Hkv query heads that read it.
+ *   q, o, dout [B, Sq, Hq, d] and k, v [B, Sk, Hkv, d] in dtype
+ *     (o and lse as written by attn_fwd for these q, k, v, scale, causal);
+ *   lse [B, Hq, Sq] fp32; dlse [B, Hq, Sq] fp32 or NULL (no LSE gradient);
+ *   dq [B, Sq, Hq, d], dk and dv [B, Sk, Hkv, d] in dtype, written whole
+ *     (keys no query sees get zero gradients).
+ * Deterministic: no atomics; dQ has its own kernel.  A per-row fp32
+ * statistics array (2 * B * Hq * ceil(Sq / 32) * 32 floats) lives in a library-owned,
+ * lazily grown workspace (released by attn_release); calls on different
+ * streams of one device share it and must not overlap.  Same validation and
+ * error codes as attn_fwd (dense only; dtype ATTN_BF16 or ATTN_FP16).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, const float* dlse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             int dtype, void* stream);
+
 /* The library's default Hadamard sign vector used by ATTN_FP8_E4M3_HADAMARD:
  * writes n (<= 128) host floats of +-1, sign i being the top bit of the
  * splitmix64 output for counter (55 << 32) + i + 1.  Returns ATTN_OK, or
@@ -228,8 +253,8 @@ int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* 
 /* Human-readable text for a status code. */
 const char* attn_strerror(int code);
 
-/* Frees the library's workspaces (fp8 operands, split-KV partials) on every
- * device that has them. */
+/* Frees the library's workspaces (fp8 operands, split-KV partials, backward
+ * statistics) on every device that has them. */
 void attn_release(void);
 
 #ifdef __cplusplus

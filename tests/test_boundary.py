@@ -172,3 +172,20 @@ def test_splitkv_and_combine_validate(lib):
     assert c(d=32) == -3
     assert c(dtype=2) == -5
     assert lib.attn_split_plan(1, 1, 1, 1, 1, 64, 0, -1, None, None, None) == -1
+
+
+def test_bwd_validates(lib):
+    def bw(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE,
+                 B=1, Hq=2, Hkv=2, Sq=64, Sk=64, d=64, scale=0.125, causal=0, dtype=0)
+        a.update(kw)
+        return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dlse"], a["dq"], a["dk"],
+                            a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"],
+                            a["causal"], a["dtype"], None)
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert bw(**{name: None}) == -1, name
+    assert bw(Sq=0) == -2 and bw(B=-1) == -2
+    assert bw(d=32) == -3
+    assert bw(Hq=3) == -4
+    assert bw(dtype=2) == -5 and bw(dtype=9) == -5
+    assert bw(scale=float("inf")) == -6
