@@ -47,33 +47,36 @@
 namespace attn {
 
 // ---------------------------------------------------------------- preprocess
-// Rows i in [Sq, Sq_pad) of the statistics get (+inf, 0): P = 0 there.
+// D/8 consecutive threads own one row (16 bytes of o and dO each, one
+// coalesced row per thread group) and sum their partial dot products with
+// shuffles.  Rows i in [Sq, Sq_pad) of the statistics get (+inf, 0): P = 0
+// there.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
+  constexpr int TPR = D / 8;                 // threads per row
   const long long rows = (long long)p.B * p.Sq_pad * p.Hq;
-  const long long rp = (long long)blockIdx.x * 256 + threadIdx.x;  // (b * Sq_pad + i) * Hq + h
-  if (rp >= rows) return;
+  const long long rp = ((long long)blockIdx.x * 256 + threadIdx.x) / TPR;   // (b * Sq_pad + i) * Hq + h
+  const int t = threadIdx.x % TPR;
+  if (rp >= rows) return;                    // whole thread groups leave together
   const int hq = (int)(rp % p.Hq);
   const long long bi = rp / p.Hq;
   const int i = (int)(bi % p.Sq_pad);
   const int b = (int)(bi / p.Sq_pad);
   const long long li = ((long long)b * p.Hq + hq) * p.Sq_pad + i;
   if (i >= p.Sq) {
-    p.stats[li] = make_float2(__builtin_inff(), 0.f);
+    if (t == 0) p.stats[li] = make_float2(__builtin_inff(), 0.f);
     return;
   }
   const long long r = ((long long)b * p.Sq + i) * p.Hq + hq;        // token-major row of o, dO
-  const T* o = (const T*)p.o + r * D;
-  const T* g = (const T*)p.dout + r * D;
+  const vec8 x = *(const vec8*)((const T*)p.o + r * D + 8 * t);
+  const vec8 y = *(const vec8*)((const T*)p.dout + r * D + 8 * t);
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const vec8 x = *(const vec8*)(o + c);
-    const vec8 y = *(const vec8*)(g + c);
+  for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
-  }
+  for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, TPR);
+  if (t != 0) return;
   const long long lo = ((long long)b * p.Hq + hq) * p.Sq + i;       // index in lse, dlse
   if (p.dlse != nullptr) acc -= p.dlse[lo];
   const float l = p.lse[lo];
@@ -126,17 +129,28 @@ struct TileCopy {
   }
 };
 
-// A operand (32 columns of block db x 16 rows of chunk cc) from a tile stored
-// with the transposed-read swizzle
-template <typename T, int D>
-__device__ __forceinline__ typename Mma<T>::vec8 read_tr(uint32_t base, const TileReads<D>& tr, int db, int cc) {
-  const uint32_t a = base + tr.voff(db) + cc * 16 * (2 * D);
-  const i16x4 lo = lds_tr16<0>(a);
-  const i16x4 hi = lds_tr16<4 * 2 * D>(a);
-  i16x4 r[2] = {lo, hi};
-  lds_wait<0>(r);
-  const i16x8 w = __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(typename Mma<T>::vec8, w);
+// Eight transposed reads (ds_read_b64_tr_b16): the A operands of two 16-row
+// chunks at each of the addresses a0 and a1 (r[2 c], r[2 c + 1] = chunk c of
+// a0; r[4 + 2 c], r[5 + 2 c] = chunk c of a1, c = 0, 1).  Wait for them with
+// lds_wait; pair j is complete once at most 6 - 2 j reads issued after it
+// are outstanding.
+template <int D>
+__device__ __forceinline__ void tr_issue8(uint32_t a0, uint32_t a1, i16x4 (&r)[8]) {
+  constexpr int R = 2 * D;
+  r[0] = lds_tr16<0>(a0);
+  r[1] = lds_tr16<4 * R>(a0);
+  r[2] = lds_tr16<16 * R>(a0);
+  r[3] = lds_tr16<20 * R>(a0);
+  r[4] = lds_tr16<0>(a1);
+  r[5] = lds_tr16<4 * R>(a1);
+  r[6] = lds_tr16<16 * R>(a1);
+  r[7] = lds_tr16<20 * R>(a1);
+}
+
+template <typename V>
+__device__ __forceinline__ V tr_pair(const i16x4 (&r)[8], int j) {
+  const i16x8 w = __builtin_shufflevector(r[2 * j], r[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(V, w);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -267,16 +281,36 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
         dsv[g >> 1][4 * (g & 1) + i] = (T)ds;
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (k = 16 queries per step)
+    // dV^T += dO^T P, dK^T += Q^T dS (k = 16 queries per step); the eight
+    // transposed reads of block db + 1 are in flight during block db's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    i16x4 tr[2][8];
+    tr_issue8<D>(stl + 3 * QT + rd.voff(0), stl + 1 * QT + rd.voff(0), tr[0]);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const vec8 ga = read_tr<T, D>(stl + 3 * QT, rd, db, cc);
-        dv[db] = Mma<T>::run(ga, pv[cc], dv[db]);
-        const vec8 qa = read_tr<T, D>(stl + 1 * QT, rd, db, cc);
-        dk[db] = Mma<T>::run(qa, dsv[cc], dk[db]);
+    for (int db = 0; db < DB; ++db) {
+      i16x4 (&cur)[8] = tr[db & 1];
+      if (db + 1 < DB) {
+        tr_issue8<D>(stl + 3 * QT + rd.voff(db + 1), stl + 1 * QT + rd.voff(db + 1), tr[(db + 1) & 1]);
+        lds_wait<14>(cur);
+        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), pv[0], dv[db]);
+        lds_wait<12>(cur);
+        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), pv[1], dv[db]);
+        lds_wait<10>(cur);
+        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[0], dk[db]);
+        lds_wait<8>(cur);
+        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[1], dk[db]);
+      } else {
+        lds_wait<6>(cur);
+        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), pv[0], dv[db]);
+        lds_wait<4>(cur);
+        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), pv[1], dv[db]);
+        lds_wait<2>(cur);
+        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[0], dk[db]);
+        lds_wait<0>(cur);
+        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[1], dk[db]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // dK^T, dV^T: lane holds key `key` and channels 32 db + 8 g + 4 h + 0..3
@@ -409,14 +443,38 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
         const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c, -l2));
         dsv[2 * bb + (r >> 3)][r & 7] = (T)(pr * (pacc[bb][r] - dl));
       }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T; chunks 0-1 and 2-3 of block db are the two halves
+    // of one eight-read batch, the next batch in flight during the MFMAs
+    static_assert(NB == 2, "four 16-key chunks per tile");
+    __builtin_amdgcn_sched_barrier(0);
+    i16x4 tr[2][8];
+    const uint32_t kt = stl + 1 * TILE;
+    tr_issue8<D>(kt + rd.voff(0), kt + rd.voff(0) + 32 * ROW, tr[0]);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int cc = 0; cc < 2 * NB; ++cc) {
-        const vec8 ka = read_tr<T, D>(stl + 1 * TILE, rd, db, cc);
-        dq[db] = Mma<T>::run(ka, dsv[cc], dq[db]);
+    for (int db = 0; db < DB; ++db) {
+      i16x4 (&cur)[8] = tr[db & 1];
+      if (db + 1 < DB) {
+        tr_issue8<D>(kt + rd.voff(db + 1), kt + rd.voff(db + 1) + 32 * ROW, tr[(db + 1) & 1]);
+        lds_wait<14>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), dsv[0], dq[db]);
+        lds_wait<12>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), dsv[1], dq[db]);
+        lds_wait<10>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[2], dq[db]);
+        lds_wait<8>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[3], dq[db]);
+      } else {
+        lds_wait<6>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), dsv[0], dq[db]);
+        lds_wait<4>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), dsv[1], dq[db]);
+        lds_wait<2>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[2], dq[db]);
+        lds_wait<0>(cur);
+        dq[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[3], dq[db]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (qi < p.Sq) {
@@ -437,8 +495,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- launch
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-  const long long rows = (long long)p.B * p.Sq_pad * p.Hq;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+  const long long threads = (long long)p.B * p.Sq_pad * p.Hq * (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int lds_kv = 2 * (4 * 32 * 2 * D + 1024);
