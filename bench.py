@@ -6,7 +6,8 @@ One step is one pass of the hot path over one batch of the workload: for the
 bf16/fp16 workloads one ``attn_fwd`` call; for the fp8 workloads the fp8
 prepass of Q, K and V plus the fp8 attention kernel; for the split-KV leg
 (decode shape) one ``attn_fwd_splitkv`` call, i.e. the split kernel and the
-combine kernel; for the backward leg one ``attn_bwd`` call.  Inputs are resident in
+combine kernel; for the backward leg one ``attn_bwd`` call; for the options
+leg one ``attn_fwd_ext`` call (softcap, then column-major V).  Inputs are resident in
 device memory before the timed region.  The timed region is bracketed by
 ``torch.cuda.synchronize()`` and measured with HIP events on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
@@ -54,6 +55,7 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workloads")
     ap.add_argument("--no-split", action="store_true", help="skip the split-KV decode leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-opts", action="store_true", help="skip the forward-options leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for the HBM byte counters)")
@@ -196,6 +198,39 @@ def splitkv_leg(ea, name, steps, warmup):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
                          "traffic": traffic_for(w.name, "splitkv", 1)}}
+
+
+def options_leg(ea, name, steps, warmup):
+    """The forward options on a dense 16-bit workload: one step = one
+    ``attn_fwd_ext`` with softcap 50 (scores capped by tanh), then with
+    column-major V; algorithmic FLOP as the plain forward's."""
+    import torch
+    import workloads as W
+    w = W.CONFIGS[name]
+    _, dev = device_inputs(w)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    vt = v.permute(0, 2, 3, 1).contiguous()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    L = ea.library()
+    st = torch.cuda.current_stream().cuda_stream
+    dt = {"bf16": ea.ATTN_BF16, "fp16": ea.ATTN_FP16}[w.dtype]
+    fl = flops_of(w)
+    out = {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.Sq} d={w.d} {w.dtype} "
+                       f"{'causal' if w.causal else 'full'}"}
+    for tag, cap, vv, vcol in (("softcap50", 50.0, v, 0), ("v_colmajor", 0.0, vt, 1)):
+        args = (q.data_ptr(), k.data_ptr(), vv.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv,
+                w.Sq, w.Sk, w.d, float(w.scale), int(w.causal), None, dt, cap, vcol, st)
+
+        def step():
+            rc = L.attn_fwd_ext(*args)
+            if rc != 0:
+                raise RuntimeError(L.attn_strerror(rc).decode())
+        ms = time_steps(step, steps, warmup) / steps
+        tf = fl / (ms * 1e-3) / 1e12
+        out[tag] = {"ms": round(ms, 5), "tflops": round(tf, 2),
+                    "pct_of_dense_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 2)}
+    return out
 
 
 def bwd_leg(ea, name, steps, warmup):
@@ -349,6 +384,8 @@ def main():
                       "c5_hadamard": fp8_leg(ea, "c5", max(5, a.steps // 5), 3, hadamard=True)}
     if not a.no_split:
         out["splitkv"] = splitkv_leg(ea, "dec", max(20, a.steps), a.warmup)
+    if not a.no_opts and W.CONFIGS[a.workload].dtype in ("bf16", "fp16") and not W.CONFIGS[a.workload].varlen:
+        out["options"] = options_leg(ea, a.workload, max(10, a.steps // 2), 3)
     if not a.no_bwd:
         out["bwd"] = bwd_leg(ea, a.workload if W.CONFIGS[a.workload].dtype in ("bf16", "fp16")
                              and not W.CONFIGS[a.workload].varlen else "c3", max(5, a.steps // 5), 3)

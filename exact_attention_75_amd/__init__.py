@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
+__all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
            "default_signs", "tile_of",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
@@ -67,6 +67,8 @@ def library() -> ctypes.CDLL:
     L.attn_split_plan.restype = I
     L.attn_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     L.attn_combine.restype = I
+    L.attn_fwd_ext.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, F, I, P]
+    L.attn_fwd_ext.restype = I
     L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     L.attn_bwd.restype = I
     L.attn_strerror.argtypes = [I]
@@ -144,6 +146,30 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     rc = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                             float(scale), int(bool(causal)), _ptr(cu_seqlens), dt, _stream())
     _check(rc, "attn_fwd")
+    return o, lse
+
+
+def fwd_ext(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            scale: Optional[float] = None, softcap: float = 0.0, v_colmajor: bool = False,
+            return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense bf16/fp16 forward with options (``attn_fwd_ext``).
+
+    q [B, Sq, Hq, d], k [B, Sk, Hkv, d]; v [B, Sk, Hkv, d], or [B, Hkv, d, Sk]
+    when v_colmajor; softcap > 0 caps the scores as softcap * tanh(s / softcap)."""
+    _need_gpu(q, k, v)
+    dt = _kernel_dtype(q, k, v)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if v_colmajor and tuple(v.shape) != (B, Hkv, d, Sk):
+        raise ValueError("column-major v must be [B, Hkv, d, Sk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = library().attn_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                                float(scale), int(bool(causal)), None, dt, float(softcap), int(bool(v_colmajor)),
+                                _stream())
+    _check(rc, "attn_fwd_ext")
     return o, lse
 
 

@@ -433,6 +433,32 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      (hipStream_t)stream);
 }
 
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                 int Sq, int Sk, int d, float scale, int causal, const int32_t* cu_seqlens, int dtype,
+                 float softcap, int v_colmajor, void* stream) {
+  if (!isfinite(softcap) || softcap < 0.f) return ATTN_ERR_ARG;
+  if (softcap == 0.f && !v_colmajor)
+    return attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, cu_seqlens, dtype, stream);
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (dtype < ATTN_BF16 || dtype > ATTN_FP8_E4M3_HADAMARD) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_ARG;   // features: 16-bit types only
+  if (cu_seqlens) return ATTN_ERR_ARG;                                  // features: dense only
+  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  if (v_colmajor && Sk % 8 != 0) return ATTN_ERR_SHAPE;                 // 16-byte aligned rows of V^T
+  attn::FwdParams p{};
+  fill_params(p, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale);
+  p.feat = (softcap > 0.f ? attn::kFeatSoftcap : 0) | (v_colmajor ? attn::kFeatVCol : 0);
+  if (softcap > 0.f) {
+    p.softcap_a = softcap / scale;
+    p.softcap_b2 = 2.f * scale * 1.4426950408889634f / softcap;
+  }
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal);
+  p.grid = p.tm.ntiles;
+  hipError_t e = attn::launch_fwd(p, dtype, d, causal, 0, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              const float* dlse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d,
              float scale, int causal, int dtype, void* stream) {

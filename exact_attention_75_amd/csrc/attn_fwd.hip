@@ -68,7 +68,15 @@ namespace attn {
 // query heads that share one KV head, row r = position * group + head in the
 // group, so that few query positions (decoding) still fill the tile and K/V
 // are fetched once for the group.  The tile map then runs over KV heads.
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT, bool PACK>
+// FEAT (dense, not split or packed; bit flags):
+//   kFeatSoftcap  scores capped as cap tanh(scale s / cap) before the mask
+//                 (attention softcapping, "FlashAttention-3 Deep Dive" API
+//                 surface); applied where each score tile is masked;
+//   kFeatVCol     V given column-major, [B, Hkv, D, Sk] (key index
+//                 innermost: the V_colmajor input, same page, FP8 layout
+//                 discussion): the PV operand is then a plain 16-byte read
+//                 of a V^T tile instead of a transposing read.
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT, bool PACK, int FEAT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -89,6 +97,9 @@ fwd_kernel(FwdParams p) {
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(BN == 64 && (BN * CPR) % (NW * 64) == 0, "tile shape");
   static_assert(!(PACK && VARLEN), "PackGQA is for dense inputs");
+  constexpr bool SOFTCAP = (FEAT & kFeatSoftcap) != 0;
+  constexpr bool VCOL = (FEAT & kFeatVCol) != 0;
+  static_assert(!VCOL || (!VARLEN && !SPLIT && !PACK), "column-major V: dense, plain tiles");
 
   // With d = 128 the Q block lives in LDS (its 32 registers per lane are
   // needed by the pipeline); with d = 64 it stays in registers.
@@ -202,10 +213,27 @@ fwd_kernel(FwdParams p) {
     const int pos = (wave_u * LOADS + i) * 64 + lane;
     const int row = pos / CPR, phys = pos % CPR;
     kdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_k<D>(row)) << 4));
-    vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+    if constexpr (VCOL) {
+      // V^T tile: D rows (channels) of BN keys = 8 chunks of 16 bytes, chunk c
+      // of row r stored at c ^ (r & 7); global rows are Sk keys apart
+      const int vr = pos / 8, vc = pos % 8;
+      vdma[i] = (uint32_t)(vr * p.Sk * 2 + ((vc ^ (vr & 7)) << 4));
+    } else {
+      vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+    }
   }
+  static_assert(!VCOL || BN * 2 == 8 * 16, "V^T tile rows of 8 chunks");
+  // column-major V: this (batch, KV head)'s [D, Sk] plane
+  const T* Vt = VCOL ? (const T*)p.v + ((long long)b * p.Hkv + hkv) * D * p.Sk : nullptr;
   auto issue = [&](const T* src, int t, char* dst, bool is_v) {
     const int j0 = t * BN;
+    if (VCOL && is_v) {
+      // range to the end of the plane: keys past Sk read the next channel's
+      // (finite) values, or zeros past the plane; their P is 0
+      const uint32_t bytes = (uint32_t)(D * p.Sk - j0) * 2u;
+      copy_rows_to_lds<LOADS>((const void*)(Vt + j0), bytes, dst + wave_u * LOADS * 1024, vdma);
+      return;
+    }
     const uint32_t bytes = (uint32_t)(kv_len - j0) * (uint32_t)ks * 2u;
     copy_rows_to_lds<LOADS>((const void*)(src + (long long)j0 * ks), bytes, dst + wave_u * LOADS * 1024,
                             is_v ? vdma : kdma);
@@ -273,13 +301,26 @@ fwd_kernel(FwdParams p) {
   const int qpos = row_pos(qi);   // causal position of the lane's query
   const char* const qwave = qsm + wave * 32 * ROW;   // this wave's Q rows (QLDS)
 
+  // column-major V: lane reads channel row 32 db + l32, keys 16 CC + 8 h .. + 7
+  // = logical chunk 2 CC + h of the row, at (2 CC + h) ^ (l32 & 7)
+  uint32_t vcol[VCOL ? 4 : 1];
+  if constexpr (VCOL) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      vcol[cc] = lds0 + STAGES * TILE + l32 * 128 + ((((2 * cc + h) ^ (l32 & 7))) << 4);
+  }
   auto read_v = [&](i16x4 (&vr)[2 * DB], uint32_t vstage, auto cc_tag) {
     constexpr int CC = decltype(cc_tag)::value;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const uint32_t a = voff(db) + vstage;
-      vr[2 * db] = lds_tr16<CC * 16 * ROW>(a);
-      vr[2 * db + 1] = lds_tr16<CC * 16 * ROW + 4 * ROW>(a);
+      if constexpr (VCOL) {
+        vr[2 * db] = lds_rd64<0>(vcol[CC] + vstage + db * 32 * 128);
+        vr[2 * db + 1] = lds_rd64<8>(vcol[CC] + vstage + db * 32 * 128);
+      } else {
+        const uint32_t a = voff(db) + vstage;
+        vr[2 * db] = lds_tr16<CC * 16 * ROW>(a);
+        vr[2 * db + 1] = lds_tr16<CC * 16 * ROW + 4 * ROW>(a);
+      }
     }
   };
 
@@ -309,6 +350,17 @@ fwd_kernel(FwdParams p) {
   };
   // mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
   auto mask = [&](int t, f32x16 (&sn)[NB]) {
+    if constexpr (SOFTCAP) {
+      // s <- (cap / scale) tanh(s scale / cap), so that c s is log2(e) times
+      // the capped score; tanh x = 1 - 2 / (e^{2x} + 1) (saturates to +-1)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e2 = __builtin_amdgcn_exp2f(sn[bb][i] * p.softcap_b2);
+          sn[bb][i] = p.softcap_a * (1.f - 2.f * __builtin_amdgcn_rcpf(e2 + 1.f));
+        }
+    }
     const int j0 = t * BN;
     const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > cw);
     if (edge) {
@@ -577,10 +629,11 @@ constexpr int fwd_lds_bytes() {
   return 2 * (NW == 8 ? 3 : 2) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
 }
 
-template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false, bool PACK = false>
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false, bool PACK = false,
+          int FEAT = 0>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   constexpr int lds = fwd_lds_bytes<D, BN, NW>();
-  auto* kern = fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT, PACK>;
+  auto* kern = fwd_kernel<T, D, BN, NW, CAUSAL, VARLEN, SPLIT, PACK, FEAT>;
   static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * NW), lds, s, p);
@@ -643,7 +696,26 @@ static bool use_wide() {
   return wide;
 }
 
+// Softcap and / or column-major V: dense 4-wave (128-row) blocks
+template <typename T, int D, int FEAT>
+static hipError_t launch_feat_t(const FwdParams& p, int causal, hipStream_t s) {
+  return causal ? launch_one<T, D, 64, 4, true, false, false, false, FEAT>(p, s)
+                : launch_one<T, D, 64, 4, false, false, false, false, FEAT>(p, s);
+}
+template <typename T, int D>
+static hipError_t launch_feat_d(const FwdParams& p, int causal, hipStream_t s) {
+  switch (p.feat) {
+    case kFeatSoftcap: return launch_feat_t<T, D, kFeatSoftcap>(p, causal, s);
+    case kFeatVCol: return launch_feat_t<T, D, kFeatVCol>(p, causal, s);
+    default: return launch_feat_t<T, D, kFeatSoftcap | kFeatVCol>(p, causal, s);
+  }
+}
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (p.feat != 0) {
+    if (dtype == 0) return d == 128 ? launch_feat_d<__bf16, 128>(p, causal, s) : launch_feat_d<__bf16, 64>(p, causal, s);
+    return d == 128 ? launch_feat_d<_Float16, 128>(p, causal, s) : launch_feat_d<_Float16, 64>(p, causal, s);
+  }
   if (p.pack && !varlen) return launch_dense4_any<false>(p, dtype, d, causal, s);
   const int bm = fwd_block_m(dtype, d, varlen);
   if (bm == 256 && d == 128 && !varlen && use_wide()) return launch_fwd_wide(p, dtype, causal, s);

@@ -107,6 +107,15 @@ __device__ __forceinline__ void lds_wait(i16x4 (&r)[N]) {
   }
 }
 
+// 8-byte LDS read issued as inline assembly (ds_read_b64), waited for like
+// lds_tr16.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_rd64(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte LDS read issued as inline assembly (ds_read_b128), for the same

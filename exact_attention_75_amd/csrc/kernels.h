@@ -11,6 +11,10 @@ namespace attn {
 
 constexpr int kBlockMMin = 128;  // smallest query block any kernel uses
 
+// Optional features of the 4-wave forward kernel (bit flags)
+constexpr int kFeatSoftcap = 1;  // scores capped: cap tanh(scale s / cap)
+constexpr int kFeatVCol = 2;     // V given column-major [B, Hkv, D, Sk]
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -35,6 +39,10 @@ struct FwdParams {
   // PackGQA (dense, 128-row blocks): tm runs over (B, Hkv, Sq * group) and a
   // tile's rows are (position, head of the group) pairs
   int pack = 0;
+  // optional features (kFeat* flags; dense, 128-row blocks, no split/pack)
+  int feat = 0;
+  float softcap_a = 0.f;      // cap / scale
+  float softcap_b2 = 0.f;     // 2 scale log2(e) / cap
 };
 
 constexpr int kCombineMaxSplits = 256;   // most partials attn_combine merges per row

@@ -141,6 +141,28 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                  float scale, int causal, void* stream);
 
 /*
+ * attn_fwd_ext -- attn_fwd with two options of the 16-bit forward
+ * ("FlashAttention-3 Deep Dive": the API surface lists attention
+ * softcapping; the FP8 layout discussion the V_colmajor input).
+ *
+ * softcap: 0 = off; > 0 replaces every score s = scale q.k by
+ *   softcap * tanh(s / softcap) before the causal mask and the softmax (the
+ *   LSE is that of the capped scores).  Must be finite and >= 0.
+ * v_colmajor: 0 = v as in attn_fwd; non-zero = v given column-major,
+ *   [B, Hkv, d, Sk] (key index innermost), which the kernel reads as the
+ *   second GEMM's operand without transposing.  Needs Sk % 8 == 0 (16-byte
+ *   aligned rows).
+ * With both options off the call is attn_fwd.  With either on: dense
+ * (cu_seqlens NULL) and dtype ATTN_BF16 / ATTN_FP16 only (else
+ * ATTN_ERR_ARG); 128-row tiles of the 4-wave kernel.  Other arguments,
+ * layouts and errors as attn_fwd.
+ */
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 const int32_t* cu_seqlens, int dtype, float softcap, int v_colmajor,
+                 void* stream);
+
+/*
  * attn_fwd_splitkv -- the dense bf16/fp16 forward of attn_fwd with the key
  * axis cut into ranges (split-KV, "flash-decoding": the Hopper tag page,
  * l1-ca0.github.io, contents 10 and 10.2.1).  Each (query tile, key range)

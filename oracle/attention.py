@@ -44,7 +44,7 @@ def _as_f64(x) -> np.ndarray:
 
 
 def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-               rows: Optional[np.ndarray] = None, key_offset: int = 0):
+               rows: Optional[np.ndarray] = None, key_offset: int = 0, softcap: float = 0.0):
     """Softmax probabilities for one head.
 
     q [Sq, d], k [Sk, d] (fp64).  Returns (P [R, Sk], m [R], l [R]) for the
@@ -52,12 +52,18 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
     P = exp(S - m) / l, S = scale * q k^T with -inf on masked entries,
     m = row max of S, l = sum_j exp(S_ij - m_i).  ``key_offset`` is the
     position of k's first row in the key sequence (for the causal mask).
+    ``softcap`` > 0 caps the scores before the mask: S = softcap *
+    tanh(scale q k^T / softcap) (attention softcapping, named in the API
+    surface of "FlashAttention-3 Deep Dive" without a formula; this is the
+    usual logit soft-capping).
     """
     Sq, Sk = q.shape[0], k.shape[0]
     if rows is None:
         rows = np.arange(Sq)
     rows = np.asarray(rows, dtype=np.int64)
     s = scale * (q[rows] @ k.T)                      # [R, Sk]
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
     if causal:
         j = key_offset + np.arange(Sk)[None, :]
         s = np.where(j > rows[:, None], -np.inf, s)
@@ -71,7 +77,8 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
 
 
 def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
-                   rows: Optional[np.ndarray] = None, row_chunk: int = 1024, key_offset: int = 0):
+                   rows: Optional[np.ndarray] = None, row_chunk: int = 1024, key_offset: int = 0,
+                   softcap: float = 0.0):
     """Attention for one head: q [Sq, d], k/v [Sk, d] -> (O [R, d], LSE [R])."""
     Sq = q.shape[0]
     if rows is None:
@@ -81,7 +88,7 @@ def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, ca
     L = np.full(len(rows), -np.inf, dtype=np.float64)
     for c0 in range(0, len(rows), row_chunk):
         r = rows[c0:c0 + row_chunk]
-        p, m, l = head_probs(q, k, scale, causal, r, key_offset)
+        p, m, l = head_probs(q, k, scale, causal, r, key_offset, softcap)
         O[c0:c0 + len(r)] = p @ v
         with np.errstate(divide="ignore"):
             L[c0:c0 + len(r)] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
@@ -90,8 +97,8 @@ def head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, ca
 
 def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None,
               heads: Optional[Sequence[int]] = None, rows: Optional[np.ndarray] = None,
-              batches: Optional[Sequence[int]] = None):
-    """Exact attention forward in fp64.
+              batches: Optional[Sequence[int]] = None, softcap: float = 0.0):
+    """Exact attention forward in fp64 (``softcap`` as in ``head_probs``).
 
     Dense:  q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d]  ->  O [B, Sq, Hq, d], LSE [B, Hq, Sq]
     Varlen: q [T, Hq, d],     k/v [T, Hkv, d], cu_seqlens [nseq+1]
@@ -113,7 +120,7 @@ def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None,
             a, b = int(cu[s]), int(cu[s + 1])
             if b <= a:
                 continue
-            o_s, l_s = attention(q[None, a:b], k[None, a:b], v[None, a:b], scale, causal)
+            o_s, l_s = attention(q[None, a:b], k[None, a:b], v[None, a:b], scale, causal, softcap=softcap)
             O[a:b] = o_s[0]
             L[:, a:b] = l_s[0]
         return O, L
@@ -131,7 +138,7 @@ def attention(q, k, v, scale: float, causal: bool = False, cu_seqlens=None,
     for b in bs:
         for h in hs:
             hk = h // group
-            o, l = head_attention(q[b, :, h], k[b, :, hk], v[b, :, hk], scale, causal, rsel)
+            o, l = head_attention(q[b, :, h], k[b, :, hk], v[b, :, hk], scale, causal, rsel, softcap=softcap)
             O[b, rsel, h] = o
             L[b, h, rsel] = l
     return O, L

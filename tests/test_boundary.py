@@ -189,3 +189,22 @@ def test_bwd_validates(lib):
     assert bw(Hq=3) == -4
     assert bw(dtype=2) == -5 and bw(dtype=9) == -5
     assert bw(scale=float("inf")) == -6
+
+
+def test_fwd_ext_validates(lib):
+    def fx(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=64, Sk=64, d=64,
+                 scale=0.125, causal=0, cu=None, dtype=0, cap=1.0, vcol=0)
+        a.update(kw)
+        return lib.attn_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                                a["Sk"], a["d"], a["scale"], a["causal"], a["cu"], a["dtype"], a["cap"],
+                                a["vcol"], None)
+    assert fx(cap=-1.0) == -6 and fx(cap=float("nan")) == -6 and fx(cap=float("inf")) == -6
+    assert fx(q=None) == -1
+    assert fx(dtype=2) == -6 and fx(dtype=3) == -6        # options: 16-bit types only
+    assert fx(dtype=11) == -5
+    assert fx(cu=FAKE) == -6                               # options: dense only
+    assert fx(cap=0.0, vcol=1, Sk=100) == -2               # column-major rows need Sk % 8 == 0
+    assert fx(d=96) == -3 and fx(Hq=3) == -4
+    # both options off: plain attn_fwd validation
+    assert fx(cap=0.0, Sq=0) == -2
