@@ -168,10 +168,14 @@ hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
 //
 // Scales: scores are sq * sk_t * (Q~ K~^T) (sq per 128 query rows, sk_t per
 // 128 keys), folded into the exp2 argument.  Probabilities are produced as
-// P' = 2^8 exp2(c s - m) <= 256 with the exact running max (no lazy
-// threshold), so they use the upper part of the E4M3 range; the 2^8 cancels
-// in O / l.  O is accumulated in units of the current V block's scale and
-// rescaled when the block changes (every second tile).
+// P' = 2^6 (sv_t / sv_max) exp2(c s - m), where sv_t is the tile's V block
+// scale and sv_max the largest V block scale of the (batch, KV head), and m
+// is a lazily updated running max: it moves only when some row's max
+// exceeds it by more than TAU = 2 (log2 units, wave-uniform decision), so
+// c s - m <= 2 and P' <= 2^8, inside the E4M3 range.  O then accumulates in
+// one unit (sv_max / 2^6) for all V blocks and is rescaled only when m
+// moves -- rarely after the first tiles.  The row sum is taken over the fp32
+// values and converted to l's units with 2^-6 sv_max / sv_t per tile.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -196,6 +200,8 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int TILE = BN * KROW;       // 8 KiB, same for V^T (D * VROW)
   constexpr int LOADS = TILE / 16 / (NW * 64);   // DMA instructions per wave per tensor
   constexpr float NEG_INF = -__builtin_inff();
+  constexpr float TAU = 2.0f;           // lazy-max threshold, log2 units
+  constexpr float POFF = 8.0f - TAU;    // log2 of P' for a probability of 1 at the running max
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];   // [K0 | K1 | V0 | V1]
 
   const int tid = threadIdx.x;
@@ -216,6 +222,10 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   const float* ksc = p.k_descale + ((long long)b * p.Hkv + hkv) * nbk;
   const float* vsc = p.v_descale + ((long long)b * p.Hkv + hkv) * nbk;
   const float sq = p.q_descale[((long long)b * p.Hq + hq) * nbq + mblk];
+  // largest V block scale of this (batch, KV head) (uniform loads)
+  float sv_max = 0.f;
+  for (int i = 0; i < nbk; ++i) sv_max = fmaxf(sv_max, vsc[i]);
+  const float lsv_max = log2f(sv_max);
 
   const int q0 = mblk * BM;
   const int qw = q0 + wave * 32;
@@ -290,7 +300,6 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = NEG_INF, l_run = 0.f;
-  float sv_cur = 0.f;     // V scale O is currently expressed in (0: none yet)
   const float cbase = p.scale_log2 * sq;
 
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
@@ -304,7 +313,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     const char* Vs = smem + (2 + (t & 1)) * TILE;
     const int j0 = t * BN;
     const float c = cbase * ksc[j0 >> 7];
-    const float sv = vsc[j0 >> 7];
+    const float lv = log2f(vsc[j0 >> 7]) - lsv_max;   // <= 0
 
     // ---- S^T = K Q^T
     f32x16 s[2];
@@ -330,7 +339,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
           s[bb][i] = dead ? NEG_INF : s[bb][i];
         }
     }
-    // ---- exact running max
+    // ---- lazy running max
     float mx = NEG_INF;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -338,17 +347,18 @@ fwd_fp8_kernel(Fp8FwdParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
     mx = fmaxf(mx, wave_half_swap(mx));
     const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0;
+    const float m_upd = moved ? m_new : m_run;
+    const float alpha = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
+    m_run = m_upd;
     const float msub = (m_run == NEG_INF) ? 0.f : m_run;
-    // O re-expressed in this tile's V scale, together with the max rescale
-    const float f = alpha * (sv_cur == 0.f ? 1.f : sv_cur / sv);
-    sv_cur = sv;
-    if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      asm volatile("" ::: "memory");   // keep the rare rescale a branch
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= f;
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
-    // ---- P' = 2^8 exp2(c s - m) -> E4M3; row sum over the fp32 values
+    // ---- P' = 2^(6 + lv) exp2(c s - m) -> E4M3; row sum over the fp32 values
+    const float off = POFF + lv - msub;
     float rs = 0.f;
     i32x8 pk;
 #pragma unroll
@@ -357,13 +367,13 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 4 * w + j;           // 0..31: block k / 16, element k % 16
-        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k >> 4][k & 15], c, 8.0f - msub));
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k >> 4][k & 15], c, off));
         rs += e[j];
       }
       int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
       pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
     }
-    l_run = l_run * alpha + rs;
+    l_run = l_run * alpha + rs * __builtin_amdgcn_exp2f(-POFF - lv);
     // ---- O^T += V^T P'^T
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -373,10 +383,10 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     }
   }
 
-  // ---- epilogue: O = O_acc * sv / l (bf16), LSE = ln2 (m - 8 + log2 l)
+  // ---- epilogue: O = O_acc sv_max / (2^6 l) (bf16), LSE = ln2 (m + log2 l)
   const float l_tot = l_run + wave_half_swap(l_run);
   if (qi < q_len) {
-    const float scl = l_tot > 0.f ? sv_cur / l_tot : 0.f;
+    const float scl = l_tot > 0.f ? sv_max / (__builtin_amdgcn_exp2f(POFF) * l_tot) : 0.f;
     __bf16* orow = (__bf16*)p.o + ((long long)b * p.Sq + qi) * qs + hq * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -389,7 +399,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
         *(bf4*)(orow + 32 * db + 8 * g + 4 * h) = w;
       }
     if (p.lse != nullptr && h == 0) {
-      const float lse = l_tot > 0.f ? (m_run - 8.0f + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+      const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
       p.lse[((long long)b * p.Hq + hq) * p.Sq + qi] = lse;
     }
   }
