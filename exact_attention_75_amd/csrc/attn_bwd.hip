@@ -336,6 +336,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
+// Per-wave software pipeline over 64-key tiles: the MFMAs of S^T_{t+1} and
+// dP^T_{t+1} carry the vector work of tile t (P = exp2(c s - lse2), masked,
+// dS = P (dP - delta), packed to 16 bits), then dQ^T += K_t^T dS_t^T.  Three
+// LDS stages: during tile t the copies of tile t + 2 are in flight, tile
+// t + 1 feeds S and dP, and tile t's transposed K copy feeds dQ.
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -345,9 +350,12 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   constexpr int DB = D / 32;
   constexpr int ROW = 2 * D;
   constexpr int TILE = BN * ROW;
+  constexpr int NST = 3;                  // LDS stages
   // stage: [K row-swizzled | K transposed-swizzled | V row-swizzled]
   constexpr int STAGE = 3 * TILE;
+  constexpr int EPS = 2 * 16 / KT;        // dS elements per k-step of the next tile's MFMAs
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  static_assert(NB == 2, "four 16-key chunks per tile");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,7 +402,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   const T* kbase = (const T*)p.k + (long long)b * p.Sk * ks + hkv * D;
   const T* vbase = (const T*)p.v + (long long)b * p.Sk * ks + hkv * D;
   auto issue = [&](int t) {
-    char* st = smem + (t & 1) * STAGE;
+    char* st = smem + (t % NST) * STAGE;
     const int j0 = t * BN;
     const uint32_t bytes = (uint32_t)(p.Sk - j0) * (uint32_t)ks * 2u;
     constexpr int L = TileCopy<D, BN, 4>::LOADS;
@@ -402,53 +410,52 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
     copy_rows_to_lds<L>(kbase + (long long)j0 * ks, bytes, st + 1 * TILE + wave * L * 1024, cp.v);
     copy_rows_to_lds<L>(vbase + (long long)j0 * ks, bytes, st + 2 * TILE + wave * L * 1024, cp.k);
   };
-  // tiles this wave needs (a causal wave stops at its diagonal); every wave
-  // still takes part in every round's barrier
+  // tiles this wave computes (a causal wave stops at its diagonal); every
+  // wave still takes part in every round's barrier
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
 
-  if (ntile > 0) issue(0);
-  for (int t = 0; t < ntile; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntile) issue(t + 1);
-    if (t >= n_w) continue;
-    const char* st = smem + (t & 1) * STAGE;
-    const uint32_t stl = lds0 + (t & 1) * STAGE;
-    const int j0 = t * BN;
-
-    // S^T = K Q^T, dP^T = V dO^T: row m of block bb is key j0 + 32 bb + key_perm(m)
-    f32x16 sacc[NB], pacc[NB];
+  // S^T and dP^T of tile t: row m of block bb is key 64 t + 32 bb + key_perm(m).
+  // step(kk) runs after the MFMAs of k-step kk.
+  auto sdp = [&](int t, f32x16 (&sa)[NB], f32x16 (&pa)[NB], auto&& step) {
+    const char* st = smem + (t % NST) * STAGE;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      sacc[bb] = f32x16{};
-      pacc[bb] = f32x16{};
-    }
-#pragma unroll
-    for (int kk = 0; kk < KT; ++kk)
+    for (int kk = 0; kk < KT; ++kk) {
+      vec8 ka[NB], va[NB];
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        const vec8 ka = *(const vec8*)(st + 0 * TILE + rd.koff(kk) + bb * 32 * ROW);
-        const vec8 va = *(const vec8*)(st + 2 * TILE + rd.koff(kk) + bb * 32 * ROW);
-        sacc[bb] = Mma<T>::run(ka, qf[kk], sacc[bb]);
-        pacc[bb] = Mma<T>::run(va, gf[kk], pacc[bb]);
+        ka[bb] = *(const vec8*)(st + 0 * TILE + rd.koff(kk) + bb * 32 * ROW);
+        va[bb] = *(const vec8*)(st + 2 * TILE + rd.koff(kk) + bb * 32 * ROW);
       }
-    // dS^T; chunk cc (16 keys) = registers 8 (cc & 1) .. + 7 of block cc >> 1
-    vec8 dsv[2 * NB];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int g = r >> 2, i = r & 3;
-        const int key = j0 + 32 * bb + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i;
-        const bool dead = (key >= p.Sk) || (CAUSAL && key > qi);
-        const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c, -l2));
-        dsv[2 * bb + (r >> 3)][r & 7] = (T)(pr * (pacc[bb][r] - dl));
+      for (int bb = 0; bb < NB; ++bb) {
+        sa[bb] = Mma<T>::run(ka[bb], qf[kk], kk == 0 ? f32x16{} : sa[bb]);
+        pa[bb] = Mma<T>::run(va[bb], gf[kk], kk == 0 ? f32x16{} : pa[bb]);
       }
-    // dQ^T += K^T dS^T; chunks 0-1 and 2-3 of block db are the two halves
-    // of one eight-read batch, the next batch in flight during the MFMAs
-    static_assert(NB == 2, "four 16-key chunks per tile");
+      step(kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // dS^T of tile t, flattened elements e0 .. e0 + n - 1 (element k: block
+  // k >> 4, register k & 15); chunk cc of 16 keys = elements 8 cc .. 8 cc + 7
+  auto ds_elems = [&](int t, const f32x16 (&sc)[NB], const f32x16 (&pc)[NB], int e0, int n, vec8 (&dsv)[2 * NB]) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int k = e0; k < e0 + n; ++k) {
+      const int bb = k >> 4, r = k & 15;
+      const int g = r >> 2, i = r & 3;
+      const int key = j0 + 32 * bb + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i;
+      const bool dead = (key >= p.Sk) || (CAUSAL && key > qi);
+      const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][r], c, -l2));
+      dsv[k >> 3][k & 7] = (T)(pr * (pc[bb][r] - dl));
+    }
+  };
+  // dQ^T += K_t^T dS_t^T (eight transposed reads per 32-channel block, the
+  // next block's in flight during the MFMAs)
+  auto dq_tile = [&](int t, const vec8 (&dsv)[2 * NB]) {
     __builtin_amdgcn_sched_barrier(0);
     i16x4 tr[2][8];
-    const uint32_t kt = stl + 1 * TILE;
+    const uint32_t kt = lds0 + (t % NST) * STAGE + 1 * TILE;
     tr_issue8<D>(kt + rd.voff(0), kt + rd.voff(0) + 32 * ROW, tr[0]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -475,7 +482,42 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // one tile: S^T, dP^T of tile t + 1 (when has_next) with dS of tile t, then dQ
+  auto tile = [&](int t, bool has_next, const f32x16 (&sc)[NB], const f32x16 (&pc)[NB], f32x16 (&sn)[NB],
+                  f32x16 (&pn)[NB]) {
+    vec8 dsv[2 * NB];
+    if (has_next) {
+      sdp(t + 1, sn, pn, [&](int kk) { ds_elems(t, sc, pc, kk * EPS, EPS, dsv); });
+    } else {
+      ds_elems(t, sc, pc, 0, 32, dsv);
+    }
+    dq_tile(t, dsv);
+  };
+  // round t: all copies landed (tile t + 1), barrier, copies of tile t + 2
+  auto top = [&](int t) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < ntile) issue(t + 2);
+  };
+
+  if (ntile > 0) issue(0);
+  if (ntile > 1) issue(1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  f32x16 sA[NB], pA[NB], sB[NB], pB[NB];
+  if (n_w > 0) sdp(0, sA, pA, [](int) {});
+  int t = 0;
+  for (; t + 1 < n_w; t += 2) {          // unrolled by two: the S / dP sets swap roles
+    top(t);
+    tile(t, true, sA, pA, sB, pB);
+    top(t + 1);
+    tile(t + 1, t + 2 < n_w, sB, pB, sA, pA);
   }
+  if (t < n_w) {
+    top(t);
+    tile(t, false, sA, pA, sB, pB);
+    ++t;
+  }
+  for (; t < ntile; ++t) top(t);
 
   if (qi < p.Sq) {
     T* dqr = (T*)p.dq + ((long long)b * p.Sq + qi) * qs + hq * D;
@@ -500,7 +542,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int lds_kv = 2 * (4 * 32 * 2 * D + 1024);
-  constexpr int lds_q = 2 * (3 * 64 * 2 * D);
+  constexpr int lds_q = 3 * (3 * 64 * 2 * D);
   static const hipError_t a1 =
       hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
   static const hipError_t a2 =
