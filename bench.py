@@ -243,26 +243,28 @@ def bwd_leg(ea, name, steps, warmup):
     from oracle.attention import attention_backward_flops  # counting rule only
     w = W.CONFIGS[name]
     _, dev = device_inputs(w)
-    q, k, v = dev["q"], dev["k"], dev["v"]
+    q, k, v, cu = dev["q"], dev["k"], dev["v"], dev["cu"]
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed_base + 7)).to(q.dtype).cuda()
-    o, lse = ea.fwd(q, k, v, causal=w.causal)
+    o, lse = ea.fwd(q, k, v, causal=w.causal, cu_seqlens=cu)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     L = ea.library()
     st = torch.cuda.current_stream().cuda_stream
     dt = {"bf16": ea.ATTN_BF16, "fp16": ea.ATTN_FP16}[w.dtype]
+    B = len(dev["lengths"]) if w.varlen else w.B
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), None,
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, float(w.scale),
-            int(w.causal), dt, st)
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, float(w.scale),
+            int(w.causal), None if cu is None else cu.data_ptr(), dt, st)
 
     def step():
         rc = L.attn_bwd(*args)
         if rc != 0:
             raise RuntimeError(L.attn_strerror(rc).decode())
     ms = time_steps(step, steps, warmup) / steps
-    fl = attention_backward_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
+    fl = 2.5 * flops_of(w, dev["lengths"]) if w.varlen else \
+        attention_backward_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
     tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.Sq} d={w.d} {w.dtype} "
-                        f"{'causal' if w.causal else 'full'} backward",
+    return {"workload": f"{w.name}: B={B} Hq={w.Hq} Hkv={w.Hkv} S={w.Sq} d={w.d} {w.dtype} "
+                        f"{'causal' if w.causal else 'full'}{' varlen' if w.varlen else ''} backward",
             "step_ms": round(ms, 5), "tflops": round(tf, 2), "algorithmic_flop_per_step": fl,
             "pct_of_dense_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 2)}
 
@@ -389,6 +391,8 @@ def main():
     if not a.no_bwd:
         out["bwd"] = bwd_leg(ea, a.workload if W.CONFIGS[a.workload].dtype in ("bf16", "fp16")
                              and not W.CONFIGS[a.workload].varlen else "c3", max(5, a.steps // 5), 3)
+        if a.workload != "c4":
+            out["bwd_varlen"] = bwd_leg(ea, "c4", max(5, a.steps // 5), 3)
     if a.extra:
         for name in ("c1", "c2", "c4"):
             if name == a.workload:

@@ -69,7 +69,7 @@ def library() -> ctypes.CDLL:
     L.attn_combine.restype = I
     L.attn_fwd_ext.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, F, I, P]
     L.attn_fwd_ext.restype = I
-    L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     L.attn_bwd.restype = I
     L.attn_strerror.argtypes = [I]
     L.attn_strerror.restype = ctypes.c_char_p
@@ -240,25 +240,35 @@ def combine(o_part: torch.Tensor, lse_part: torch.Tensor, dtype: torch.dtype = t
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         do: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
-        dlse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Attention backward through ``attn_bwd`` (dense bf16/fp16).
+        dlse: Optional[torch.Tensor] = None,
+        cu_seqlens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Attention backward through ``attn_bwd`` (bf16/fp16).
 
-    q, o, do [B, Sq, Hq, d]; k, v [B, Sk, Hkv, d]; lse (and the optional LSE
-    gradient dlse) fp32 [B, Hq, Sq] -> dq [B, Sq, Hq, d], dk, dv [B, Sk, Hkv, d]."""
-    _need_gpu(q, k, v, o, lse, do, dlse)
+    Dense: q, o, do [B, Sq, Hq, d]; k, v [B, Sk, Hkv, d]; lse (and the optional
+    LSE gradient dlse) fp32 [B, Hq, Sq] -> dq [B, Sq, Hq, d], dk, dv [B, Sk, Hkv, d].
+    Varlen (cu_seqlens int32 [nseq+1]): q, o, do [T, Hq, d]; k, v [T, Hkv, d];
+    lse, dlse [Hq, T]."""
+    _need_gpu(q, k, v, o, lse, do, dlse, cu_seqlens)
     dt = _kernel_dtype(q, k, v, o, do)
     if lse.dtype != torch.float32 or (dlse is not None and dlse.dtype != torch.float32):
         raise ValueError("lse and dlse must be fp32")
-    B, Sq, Hq, d = q.shape
-    Sk, Hkv = k.shape[1], k.shape[2]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        B, Sq, Sk = cu_seqlens.numel() - 1, T, k.shape[0]
+    else:
+        B, Sq, Hq, d = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     rc = library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dlse), _ptr(dq),
-                            _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), dt,
-                            _stream())
+                            _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)),
+                            _ptr(cu_seqlens), dt, _stream())
     _check(rc, "attn_bwd")
     return dq, dk, dv
 

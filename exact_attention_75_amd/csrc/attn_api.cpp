@@ -461,16 +461,25 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              const float* dlse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d,
-             float scale, int causal, int dtype, void* stream) {
+             float scale, int causal, const int32_t* cu_seqlens, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
-  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    if (B <= 0) return ATTN_ERR_SHAPE;
+    if (Sq != Sk) return ATTN_ERR_SHAPE;
+  }
+  int rc = check_common(varlen ? 1 : B, Hq, Hkv, Sq, Sk, d, scale);
   if (rc) return rc;
-  const long long nkb = (Sk + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
-  if ((long long)B * Hkv * nkb > kMax32) return ATTN_ERR_SIZE;
-  const int sq_pad = (Sq + 31) / 32 * 32;
+  // dK/dV workgroups: (batch, KV head, 128 keys); varlen: at most
+  // ceil(T / 128) + (number of sequences) key blocks per KV head
+  const long long nkb = varlen ? (Sk + attn::kBwdBlockN - 1) / attn::kBwdBlockN + B
+                               : (long long)B * ((Sk + attn::kBwdBlockN - 1) / attn::kBwdBlockN);
+  const long long nqb = varlen ? (Sq + attn::kBwdBlockM - 1) / attn::kBwdBlockM + B : 0;
+  if ((long long)Hkv * nkb > kMax32 || (long long)Hq * nqb > kMax32) return ATTN_ERR_SIZE;
+  const int sq_pad = varlen ? Sq : (Sq + 31) / 32 * 32;
   void* ws = nullptr;
-  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)B * Hq * sq_pad, &ws);
+  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)(varlen ? 1 : B) * Hq * sq_pad, &ws);
   if (rc) return rc;
   attn::BwdParams p{};
   p.q = q;
@@ -484,6 +493,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.dk = dk;
   p.dv = dv;
   p.stats = (float2*)ws;
+  p.cu_seqlens = cu_seqlens;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -493,10 +503,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.group = Hq / Hkv;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBwdBlockM, causal);
-  p.grid_dq = p.tm.ntiles;
-  p.grid_dkdv = (int)(B * Hkv * nkb);
-  hipError_t e = attn::launch_bwd(p, dtype, d, causal, (hipStream_t)stream);
+  if (varlen) {
+    p.grid_dq = (int)(Hq * nqb);
+  } else {
+    p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::kBwdBlockM, causal);
+    p.grid_dq = p.tm.ntiles;
+  }
+  p.grid_dkdv = (int)(Hkv * nkb);
+  hipError_t e = attn::launch_bwd(p, dtype, d, causal, varlen ? 1 : 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

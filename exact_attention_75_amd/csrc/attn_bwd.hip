@@ -154,7 +154,10 @@ __device__ __forceinline__ V tr_pair(const i16x4 (&r)[8], int j) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <typename T, int D, bool CAUSAL>
+// VARLEN: p.B sequences packed along the token axis (cu_seqlens); workgroup
+// = (KV head, sequence, key block), the statistics read directly from global
+// memory (their per-sequence rows are not 16-byte aligned for the copy).
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
   constexpr int BMQ = 32;                 // query rows per step
@@ -175,19 +178,43 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
 
   // key blocks in ascending order first: with causal masking the first ones
   // see the most queries (longest first)
-  const int G = p.B * p.Hkv;
-  const int nblk = blockIdx.x / G;
-  const int gi = blockIdx.x % G;
-  const int b = gi / p.Hkv, hkv = gi % p.Hkv;
+  int b, hkv, nblk, q_len, k_len;
+  long long q_tok0, k_tok0;               // token index of the sequence's first query / key
+  if constexpr (VARLEN) {
+    hkv = blockIdx.x % p.Hkv;
+    int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
+    for (; sq < p.B; ++sq) {
+      start = p.cu_seqlens[sq];
+      len = p.cu_seqlens[sq + 1] - start;
+      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
+      if (r < nb) break;
+      r -= nb;
+    }
+    if (sq >= p.B) return;                // beyond the last block (uniform over the workgroup)
+    b = 0;
+    nblk = r;
+    q_len = k_len = len;
+    q_tok0 = k_tok0 = start;
+  } else {
+    const int G = p.B * p.Hkv;
+    nblk = blockIdx.x / G;
+    const int gi = blockIdx.x % G;
+    b = gi / p.Hkv;
+    hkv = gi % p.Hkv;
+    q_len = p.Sq;
+    k_len = p.Sk;
+    q_tok0 = (long long)b * p.Sq;
+    k_tok0 = (long long)b * p.Sk;
+  }
   const int k0 = nblk * kBwdBlockN;
-  const int key = k0 + wave * 32 + l32;   // this lane's key (column of S)
+  const int key = k0 + wave * 32 + l32;   // this lane's key (column of S), sequence position
   const int qs = p.Hq * D;                // token stride of q, o, dO, dQ
 
   // K and V of the lane's key as B operands (k = head dimension); rows past
   // the end read a valid row and are masked
   vec8 kf[KT], vf[KT];
   {
-    const long long row = ((long long)b * p.Sk + min(key, p.Sk - 1)) * p.Hkv + hkv;
+    const long long row = (k_tok0 + min(key, k_len - 1)) * p.Hkv + hkv;
     const T* kr = (const T*)p.k + row * D + 8 * h;
     const T* vr = (const T*)p.v + row * D + 8 * h;
 #pragma unroll
@@ -203,7 +230,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     dk[i] = f32x16{};
   }
 
-  const int nM = (p.Sq + BMQ - 1) / BMQ;
+  const int nM = (q_len + BMQ - 1) / BMQ;
   const int m_begin = CAUSAL ? min(k0 / BMQ, nM) : 0;   // queries before k0 see none of these keys
   const int per_head = nM - m_begin;
   const int nsteps = p.group * per_head;
@@ -221,8 +248,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     int hq, q0;
     step_coords(s, hq, q0);
     char* st = smem + (s & 1) * STAGE;
-    const long long off = ((long long)b * p.Sq + q0) * qs + hq * D;
-    const uint32_t bytes = (uint32_t)(p.Sq - q0) * (uint32_t)qs * 2u;
+    const long long off = (q_tok0 + q0) * qs + hq * D;
+    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
     const T* qb = (const T*)p.q + off;
     const T* gb = (const T*)p.dout + off;
     constexpr int L = TileCopy<D, BMQ, 4>::LOADS;
@@ -230,7 +257,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
     copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
     copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
-    if (wave == 0) {
+    if (!VARLEN && wave == 0) {
       // 32 (lse2, delta) pairs = 16 lanes x 16 bytes (the array is padded to
       // 32 rows per head, so no 16-byte read straddles its end); the other
       // lanes' offsets are out of range and write zeros past the pairs
@@ -246,7 +273,6 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     if (s + 1 < nsteps) issue(s + 1);
     int hq, q0;
     step_coords(s, hq, q0);
-    (void)hq;
     const char* st = smem + (s & 1) * STAGE;
     const uint32_t stl = lds0 + (s & 1) * STAGE;
 
@@ -261,20 +287,33 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     }
     // register r = 4 g + i holds query 16 (g >> 1) + 8 h + 4 (g & 1) + i:
     // 4 consecutive queries per g, read as 2 x 16 bytes of (lse2, delta)
+    // (varlen: from global memory, rows past the sequence clamped to its last
+    // row -- their Q and dO are zero, so they contribute nothing)
     const float* sp = (const float*)(st + 4 * QT);
+    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;   // varlen layout [Hq, T]
     vec8 pv[2], dsv[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qr = 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-      const float4 s01 = *(const float4*)(sp + 2 * qr);
-      const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
-      const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
-      const float dl[4] = {s01.y, s01.w, s23.y, s23.w};
+      float l2[4], dl[4];
+      if constexpr (VARLEN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 v2 = sg[min(q0 + qr + i, q_len - 1)];
+          l2[i] = v2.x;
+          dl[i] = v2.y;
+        }
+      } else {
+        const float4 s01 = *(const float4*)(sp + 2 * qr);
+        const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
+        l2[0] = s01.x; l2[1] = s01.z; l2[2] = s23.x; l2[3] = s23.z;
+        dl[0] = s01.y; dl[1] = s01.w; dl[2] = s23.y; dl[3] = s23.w;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         const int qrow = q0 + qr + i;
-        const bool dead = (key >= p.Sk) || (CAUSAL && key > qrow);
+        const bool dead = (key >= k_len) || (CAUSAL && key > qrow);
         const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2[i]));
         const float ds = pr * (pacc[r] - dl[i]);
         pv[g >> 1][4 * (g & 1) + i] = (T)pr;
@@ -314,8 +353,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   }
 
   // dK^T, dV^T: lane holds key `key` and channels 32 db + 8 g + 4 h + 0..3
-  if (key < p.Sk) {
-    const long long row = ((long long)b * p.Sk + key) * p.Hkv + hkv;
+  if (key < k_len) {
+    const long long row = (k_tok0 + key) * p.Hkv + hkv;
     T* dkr = (T*)p.dk + row * D;
     T* dvr = (T*)p.dv + row * D;
     typedef T T4 __attribute__((ext_vector_type(4)));
@@ -341,7 +380,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
 // dS = P (dP - delta), packed to 16 bits), then dQ^T += K_t^T dS_t^T.  Three
 // LDS stages: during tile t the copies of tile t + 2 are in flight, tile
 // t + 1 feeds S and dP, and tile t's transposed K copy feeds dQ.
-template <typename T, int D, bool CAUSAL>
+// VARLEN: workgroup = (query head, sequence, 128-row block), longest block of
+// a sequence first.
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
   constexpr int BN = 64;                  // keys per tile
@@ -363,23 +404,47 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  int b, hq, mblk;
-  tile_decode(p.tm, (int)blockIdx.x, b, hq, mblk);
+  int b, hq, mblk, q_len, k_len;
+  long long q_tok0, k_tok0, stat0;        // first query / key token; stats index of query 0
+  if constexpr (VARLEN) {
+    hq = blockIdx.x % p.Hq;
+    int r = blockIdx.x / p.Hq, sq = 0, start = 0, len = 0, nb = 0;
+    for (; sq < p.B; ++sq) {
+      start = p.cu_seqlens[sq];
+      len = p.cu_seqlens[sq + 1] - start;
+      nb = (len + kBwdBlockM - 1) / kBwdBlockM;
+      if (r < nb) break;
+      r -= nb;
+    }
+    if (sq >= p.B) return;                // beyond the last tile (uniform over the workgroup)
+    b = 0;
+    mblk = nb - 1 - r;                    // longest query block of the sequence first
+    q_len = k_len = len;
+    q_tok0 = k_tok0 = start;
+    stat0 = (long long)hq * p.Sq + start;   // varlen layout [Hq, T]
+  } else {
+    tile_decode(p.tm, (int)blockIdx.x, b, hq, mblk);
+    q_len = p.Sq;
+    k_len = p.Sk;
+    q_tok0 = (long long)b * p.Sq;
+    k_tok0 = (long long)b * p.Sk;
+    stat0 = ((long long)b * p.Hq + hq) * p.Sq_pad;
+  }
   const int hkv = hq / p.group;
   const int qs = p.Hq * D;
   const int ks = p.Hkv * D;
   const int q0 = mblk * kBwdBlockM;
   const int qw = q0 + wave * 32;
   const int qi = qw + key_perm(l32);      // this lane's query (column of S^T)
-  const int qc = min(qi, p.Sq - 1);       // rows past the end compute on a valid row, never stored
-  const int q_hi = min(q0 + kBwdBlockM, p.Sq);
-  const int kv_end = CAUSAL ? min(p.Sk, q_hi) : p.Sk;
+  const int qc = min(qi, q_len - 1);      // rows past the end compute on a valid row, never stored
+  const int q_hi = min(q0 + kBwdBlockM, q_len);
+  const int kv_end = CAUSAL ? min(k_len, q_hi) : k_len;
   const int ntile = (kv_end + BN - 1) / BN;
 
   // Q and dO of the lane's query as B operands (k = head dimension)
   vec8 qf[KT], gf[KT];
   {
-    const long long row = ((long long)b * p.Sq + qc) * p.Hq + hq;
+    const long long row = (q_tok0 + qc) * p.Hq + hq;
     const T* qr = (const T*)p.q + row * D + 8 * h;
     const T* gr = (const T*)p.dout + row * D + 8 * h;
 #pragma unroll
@@ -388,7 +453,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
       gf[kk] = *(const vec8*)(gr + 16 * kk);
     }
   }
-  const float2 st2 = p.stats[((long long)b * p.Hq + hq) * p.Sq_pad + qc];
+  const float2 st2 = p.stats[stat0 + qc];
   const float l2 = st2.x, dl = st2.y;
   const float c = p.scale_log2;
 
@@ -399,12 +464,12 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   const TileCopy<D, BN, 4> cp(wave, lane, ks);
   const TileReads<D> rd(lane);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
-  const T* kbase = (const T*)p.k + (long long)b * p.Sk * ks + hkv * D;
-  const T* vbase = (const T*)p.v + (long long)b * p.Sk * ks + hkv * D;
+  const T* kbase = (const T*)p.k + k_tok0 * ks + hkv * D;
+  const T* vbase = (const T*)p.v + k_tok0 * ks + hkv * D;
   auto issue = [&](int t) {
     char* st = smem + (t % NST) * STAGE;
     const int j0 = t * BN;
-    const uint32_t bytes = (uint32_t)(p.Sk - j0) * (uint32_t)ks * 2u;
+    const uint32_t bytes = (uint32_t)(k_len - j0) * (uint32_t)ks * 2u;
     constexpr int L = TileCopy<D, BN, 4>::LOADS;
     copy_rows_to_lds<L>(kbase + (long long)j0 * ks, bytes, st + 0 * TILE + wave * L * 1024, cp.k);
     copy_rows_to_lds<L>(kbase + (long long)j0 * ks, bytes, st + 1 * TILE + wave * L * 1024, cp.v);
@@ -445,7 +510,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
       const int bb = k >> 4, r = k & 15;
       const int g = r >> 2, i = r & 3;
       const int key = j0 + 32 * bb + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i;
-      const bool dead = (key >= p.Sk) || (CAUSAL && key > qi);
+      const bool dead = (key >= k_len) || (CAUSAL && key > qi);
       const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][r], c, -l2));
       dsv[k >> 3][k & 7] = (T)(pr * (pc[bb][r] - dl));
     }
@@ -519,8 +584,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   }
   for (; t < ntile; ++t) top(t);
 
-  if (qi < p.Sq) {
-    T* dqr = (T*)p.dq + ((long long)b * p.Sq + qi) * qs + hq * D;
+  if (qi < q_len) {
+    T* dqr = (T*)p.dq + (q_tok0 + qi) * qs + hq * D;
     typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -535,35 +600,42 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-  const long long threads = (long long)p.B * p.Sq_pad * p.Hq * (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+  // the preprocess sees a varlen batch as one sequence of T tokens ([Hq, T])
+  BwdParams pp = p;
+  if (VARLEN) {
+    pp.B = 1;
+    pp.Sq_pad = p.Sq;
+  }
+  const long long threads = (long long)pp.B * pp.Sq_pad * pp.Hq * (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int lds_kv = 2 * (4 * 32 * 2 * D + 1024);
   constexpr int lds_q = 3 * (3 * 64 * 2 * D);
-  static const hipError_t a1 =
-      hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
-  static const hipError_t a2 =
-      hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
+  static const hipError_t a1 = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+  static const hipError_t a2 = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, CAUSAL, VARLEN>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(p.grid_dkdv), dim3(256), lds_kv, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds_kv, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(p.grid_dq), dim3(256), lds_q, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dq), dim3(256), lds_q, s, p);
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_bwd_d(const BwdParams& p, int d, int causal, hipStream_t s) {
-  if (d == 128) return causal ? launch_bwd_t<T, 128, true>(p, s) : launch_bwd_t<T, 128, false>(p, s);
-  return causal ? launch_bwd_t<T, 64, true>(p, s) : launch_bwd_t<T, 64, false>(p, s);
+template <typename T, int D>
+static hipError_t launch_bwd_v(const BwdParams& p, int causal, int varlen, hipStream_t s) {
+  if (varlen) return causal ? launch_bwd_t<T, D, true, true>(p, s) : launch_bwd_t<T, D, false, true>(p, s);
+  return causal ? launch_bwd_t<T, D, true, false>(p, s) : launch_bwd_t<T, D, false, false>(p, s);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, hipStream_t s) {
-  return dtype == 0 ? launch_bwd_d<__bf16>(p, d, causal, s) : launch_bwd_d<_Float16>(p, d, causal, s);
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (dtype == 0) return d == 128 ? launch_bwd_v<__bf16, 128>(p, causal, varlen, s) : launch_bwd_v<__bf16, 64>(p, causal, varlen, s);
+  return d == 128 ? launch_bwd_v<_Float16, 128>(p, causal, varlen, s) : launch_bwd_v<_Float16, 64>(p, causal, varlen, s);
 }
 
 }  // namespace attn

@@ -66,7 +66,8 @@ struct BwdParams {
   void* dq;                   // [B, Sq, Hq, D]
   void* dk;                   // [B, Sk, Hkv, D]
   void* dv;                   // [B, Sk, Hkv, D]
-  float2* stats;              // [B, Hq, Sq_pad]: (LSE * log2 e, or +inf for -inf; delta)
+  float2* stats;              // [B, Hq, Sq_pad] ([Hq, T] varlen): (LSE log2 e, or +inf for -inf; delta)
+  const int32_t* cu_seqlens;  // varlen offsets (device) or nullptr; then B = sequences, Sq = Sk = T
   int B, Hq, Hkv, Sq, Sk;
   int Sq_pad;                 // Sq rounded up to 32 (rows past Sq: (+inf, 0))
   int group;
@@ -120,7 +121,7 @@ hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s);
 // Backward: statistics preprocess, dK/dV (parallel over key blocks), dQ
 // (parallel over query blocks); dense bf16/fp16, d in {64, 128}.
-hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
 constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);

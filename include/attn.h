@@ -232,7 +232,7 @@ int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse
                  int B, int Hq, int Sq, int d, int dtype, void* stream);
 
 /*
- * attn_bwd -- attention backward (bf16 / fp16, dense, d = 64 or 128).
+ * attn_bwd -- attention backward (bf16 / fp16, dense or varlen, d = 64 or 128).
  *
  * Gradients of O = softmax(scale Q K^T + mask) V (and of LSE when dlse is
  * given), by the chain rule listed in the Hopper tag page (l1-ca0.github.io,
@@ -245,16 +245,20 @@ int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse
  *   lse [B, Hq, Sq] fp32; dlse [B, Hq, Sq] fp32 or NULL (no LSE gradient);
  *   dq [B, Sq, Hq, d], dk and dv [B, Sk, Hkv, d] in dtype, written whole
  *     (keys no query sees get zero gradients).
+ * Varlen (cu_seqlens != NULL): as for attn_fwd -- B sequences packed along
+ *   the token axis, Sq == Sk == T; q, o, dout, dq [T, Hq, d], k, v, dk, dv
+ *   [T, Hkv, d], lse and dlse [Hq, T]; sequences do not see each other.
  * Deterministic: no atomics; dQ has its own kernel.  A per-row fp32
- * statistics array (2 * B * Hq * ceil(Sq / 32) * 32 floats) lives in a library-owned,
+ * statistics array (2 * B * Hq * ceil(Sq / 32) * 32 floats; varlen 2 * Hq * T)
+ * lives in a library-owned,
  * lazily grown workspace (released by attn_release); calls on different
  * streams of one device share it and must not overlap.  Same validation and
- * error codes as attn_fwd (dense only; dtype ATTN_BF16 or ATTN_FP16).
+ * error codes as attn_fwd (dtype ATTN_BF16 or ATTN_FP16).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, const float* dlse, void* dq, void* dk, void* dv,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
-             int dtype, void* stream);
+             const int32_t* cu_seqlens, int dtype, void* stream);
 
 /* The library's default Hadamard sign vector used by ATTN_FP8_E4M3_HADAMARD:
  * writes n (<= 128) host floats of +-1, sign i being the top bit of the

@@ -177,11 +177,11 @@ def test_splitkv_and_combine_validate(lib):
 def test_bwd_validates(lib):
     def bw(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE,
-                 B=1, Hq=2, Hkv=2, Sq=64, Sk=64, d=64, scale=0.125, causal=0, dtype=0)
+                 B=1, Hq=2, Hkv=2, Sq=64, Sk=64, d=64, scale=0.125, causal=0, cu=None, dtype=0)
         a.update(kw)
         return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dlse"], a["dq"], a["dk"],
                             a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"],
-                            a["causal"], a["dtype"], None)
+                            a["causal"], a["cu"], a["dtype"], None)
     for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
         assert bw(**{name: None}) == -1, name
     assert bw(Sq=0) == -2 and bw(B=-1) == -2
@@ -189,6 +189,7 @@ def test_bwd_validates(lib):
     assert bw(Hq=3) == -4
     assert bw(dtype=2) == -5 and bw(dtype=9) == -5
     assert bw(scale=float("inf")) == -6
+    assert bw(cu=FAKE, Sk=65) == -2 and bw(cu=FAKE, B=0) == -2   # varlen needs Sq == Sk, B > 0
 
 
 def test_fwd_ext_validates(lib):

@@ -162,3 +162,53 @@ def test_bwd_full_size_sampled(ea, name):
     compare("dq", sl(dq, hs), rq, f"full {name}")
     compare("dk", sl(dk, [hkv]), rk, f"full {name}")
     compare("dv", sl(dv, [hkv]), rv, f"full {name}")
+
+
+def varlen_inputs(lens, Hq, Hkv, d, dtype, seed, causal):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = W.make_dense(1, T, T, Hq, Hkv, d, dtype, seed=seed)
+    q, k, v = q[0], k[0], v[0]
+    g = torch.Generator().manual_seed(seed + 1000)
+    do = torch.randn(T, Hq, d, generator=g).to(q.dtype)
+    o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal, cu_seqlens=cu)
+    return cu, q, k, v, do, torch.from_numpy(o_ref).to(q.dtype), torch.from_numpy(l_ref).float()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens", [[100, 0, 300, 1, 129], [256], [33, 500, 64]])
+def test_bwd_varlen(ea, dtype, d, causal, lens):
+    print(f"[case] bwd varlen dtype={dtype} d={d} causal={causal} lens={lens}", flush=True)
+    cu, q, k, v, do, o, lse = varlen_inputs(lens, 4, 2, d, dtype, sum(lens) + d, causal)
+    dev = [t.cuda() for t in (q, k, v, o, lse, do)]
+    dq, dk, dv = ea.bwd(*dev, causal=causal, cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    rq, rk, rv = A.attention_backward(q, k, v, do, 1 / math.sqrt(d), causal, cu_seqlens=cu)
+    tag = f"bwd varlen {dtype} d{d} c{int(causal)} {lens}"
+    compare("dq", dq, rq, tag)
+    compare("dk", dk, rk, tag)
+    compare("dv", dv, rv, tag)
+
+
+def test_bwd_varlen_c4_sampled_heads(ea):
+    # c4's packed batch (10 sequences, fp16, d = 64, causal): the GPU computes
+    # every head, the oracle heads 0 and 15 over all sequences
+    w = W.CONFIGS["c4"]
+    inp = W.make_inputs(w)
+    cu = inp["cu_seqlens"]
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(47)).to(q.dtype)
+    cuc = torch.from_numpy(cu).cuda()
+    qc, kc, vc, gc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    print("[case] bwd varlen c4", flush=True)
+    o, lse = ea.fwd(qc, kc, vc, causal=True, cu_seqlens=cuc)
+    dq, dk, dv = ea.bwd(qc, kc, vc, o, lse, gc, causal=True, cu_seqlens=cuc)
+    torch.cuda.synchronize()
+    for h in (0, 15):
+        sl = lambda t: t[:, h:h + 1]
+        rq, rk, rv = A.attention_backward(sl(q), sl(k), sl(v), sl(do), w.scale, True, cu_seqlens=cu)
+        compare("dq", sl(dq), rq, f"c4 head {h}")
+        compare("dk", sl(dk), rk, f"c4 head {h}")
+        compare("dv", sl(dv), rv, f"c4 head {h}")
