@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip",
+           "attn_bwd_dkdv.hip"]
 ARCH = "gfx950"
 
 
@@ -64,7 +65,7 @@ def compile_one(src: str, save_temps: str | None) -> str:
 
 # Sources whose kernels keep data in AGPRs named in inline assembly: the
 # compiler must not use any AGPR itself there (see csrc/wide_regs.h).
-PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip"]
+PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip", "attn_bwd_dkdv.hip"]
 
 
 def check_pinned_agprs(src: str) -> None:

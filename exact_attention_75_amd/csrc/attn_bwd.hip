@@ -41,6 +41,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "bwd_common.h"
 #include "kernel_common.h"
 #include "kernels.h"
 
@@ -83,295 +86,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   // a row that saw no key has LSE = -inf and P = 0: +inf makes exp2 give 0
   const float l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * 1.4426950408889634f;
   p.stats[li] = make_float2(l2, acc);
-}
-
-// Per-lane LDS byte offsets of the two read patterns over a tile of rows of
-// D 16-bit elements (row stride 2 D bytes):
-//   row reads  (A/B operand, 8 consecutive elements of row key_perm(l % 32)):
-//              koff(kk) = koff0 ^ (kk << 5), +32 rows per 32-row block;
-//   transposed (A operand: 32 columns x 16 rows, ds_read_b64_tr_b16 pairs):
-//              voff(db) = voff0 ^ (db << 6), + 16 rows per chunk, second
-//              read + 4 rows.
-template <int D>
-struct TileReads {
-  static constexpr int ROW = 2 * D;
-  int koff0;
-  uint32_t voff0;
-  __device__ __forceinline__ TileReads(int lane) {
-    const int h = lane >> 5, l32 = lane & 31;
-    const int r0 = key_perm(l32);
-    koff0 = r0 * ROW + ((h ^ swz_k<D>(r0)) << 4);
-    const int G = lane >> 4, i16 = lane & 15;
-    const int r = 8 * h + (i16 >> 2);
-    const int dd = 16 * (G & 1) + 4 * (i16 & 3);
-    voff0 = r * ROW + (((dd >> 3) ^ swz_v<D>(r)) << 4) + ((dd & 7) << 1);
-  }
-  __device__ __forceinline__ int koff(int kk) const { return koff0 ^ (kk << 5); }
-  __device__ __forceinline__ uint32_t voff(int db) const { return voff0 ^ (uint32_t)(db << 6); }
-};
-
-// DMA offsets of the copy of a tile of ROWS rows (row stride `stride`
-// elements in global memory) by NW waves, for either swizzle.
-template <int D, int ROWS, int NW>
-struct TileCopy {
-  static constexpr int CPR = D / 8;
-  static constexpr int LOADS = ROWS * CPR / (NW * 64);
-  static_assert(LOADS >= 1 && ROWS * CPR % (NW * 64) == 0, "tile copy shape");
-  uint32_t k[LOADS], v[LOADS];
-  __device__ __forceinline__ TileCopy(int wave, int lane, int stride) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int pos = (wave * LOADS + i) * 64 + lane;
-      const int row = pos / CPR, phys = pos % CPR;
-      k[i] = (uint32_t)(row * stride * 2 + ((phys ^ swz_k<D>(row)) << 4));
-      v[i] = (uint32_t)(row * stride * 2 + ((phys ^ swz_v<D>(row)) << 4));
-    }
-  }
-};
-
-// Eight transposed reads (ds_read_b64_tr_b16): the A operands of two 16-row
-// chunks at each of the addresses a0 and a1 (r[2 c], r[2 c + 1] = chunk c of
-// a0; r[4 + 2 c], r[5 + 2 c] = chunk c of a1, c = 0, 1).  Wait for them with
-// lds_wait; pair j is complete once at most 6 - 2 j reads issued after it
-// are outstanding.
-template <int D>
-__device__ __forceinline__ void tr_issue8(uint32_t a0, uint32_t a1, i16x4 (&r)[8]) {
-  constexpr int R = 2 * D;
-  r[0] = lds_tr16<0>(a0);
-  r[1] = lds_tr16<4 * R>(a0);
-  r[2] = lds_tr16<16 * R>(a0);
-  r[3] = lds_tr16<20 * R>(a0);
-  r[4] = lds_tr16<0>(a1);
-  r[5] = lds_tr16<4 * R>(a1);
-  r[6] = lds_tr16<16 * R>(a1);
-  r[7] = lds_tr16<20 * R>(a1);
-}
-
-template <typename V>
-__device__ __forceinline__ V tr_pair(const i16x4 (&r)[8], int j) {
-  const i16x8 w = __builtin_shufflevector(r[2 * j], r[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(V, w);
-}
-
-// ---------------------------------------------------------------- dK, dV
-// VARLEN: p.B sequences packed along the token axis (cu_seqlens); workgroup
-// = (KV head, sequence, key block), the statistics read directly from global
-// memory (their per-sequence rows are not 16-byte aligned for the copy).
-template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
-  typedef typename Mma<T>::vec8 vec8;
-  constexpr int BMQ = 32;                 // query rows per step
-  constexpr int KT = D / 16;              // k-steps over the head dimension
-  constexpr int DB = D / 32;              // 32-column blocks of dK^T, dV^T
-  constexpr int ROW = 2 * D;
-  constexpr int QT = BMQ * ROW;           // one 32-row tile
-  constexpr int STAT = 1024;              // (lse2, delta) of 32 rows, in a 1 KiB slot
-  // stage: [Q row-swizzled | Q transposed-swizzled | dO row | dO transposed | stats]
-  constexpr int STAGE = 4 * QT + STAT;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  // key blocks in ascending order first: with causal masking the first ones
-  // see the most queries (longest first)
-  int b, hkv, nblk, q_len, k_len;
-  long long q_tok0, k_tok0;               // token index of the sequence's first query / key
-  if constexpr (VARLEN) {
-    hkv = blockIdx.x % p.Hkv;
-    int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
-    for (; sq < p.B; ++sq) {
-      start = p.cu_seqlens[sq];
-      len = p.cu_seqlens[sq + 1] - start;
-      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
-      if (r < nb) break;
-      r -= nb;
-    }
-    if (sq >= p.B) return;                // beyond the last block (uniform over the workgroup)
-    b = 0;
-    nblk = r;
-    q_len = k_len = len;
-    q_tok0 = k_tok0 = start;
-  } else {
-    const int G = p.B * p.Hkv;
-    nblk = blockIdx.x / G;
-    const int gi = blockIdx.x % G;
-    b = gi / p.Hkv;
-    hkv = gi % p.Hkv;
-    q_len = p.Sq;
-    k_len = p.Sk;
-    q_tok0 = (long long)b * p.Sq;
-    k_tok0 = (long long)b * p.Sk;
-  }
-  const int k0 = nblk * kBwdBlockN;
-  const int key = k0 + wave * 32 + l32;   // this lane's key (column of S), sequence position
-  const int qs = p.Hq * D;                // token stride of q, o, dO, dQ
-
-  // K and V of the lane's key as B operands (k = head dimension); rows past
-  // the end read a valid row and are masked
-  vec8 kf[KT], vf[KT];
-  {
-    const long long row = (k_tok0 + min(key, k_len - 1)) * p.Hkv + hkv;
-    const T* kr = (const T*)p.k + row * D + 8 * h;
-    const T* vr = (const T*)p.v + row * D + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < KT; ++kk) {
-      kf[kk] = *(const vec8*)(kr + 16 * kk);
-      vf[kk] = *(const vec8*)(vr + 16 * kk);
-    }
-  }
-  f32x16 dv[DB], dk[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dv[i] = f32x16{};
-    dk[i] = f32x16{};
-  }
-
-  const int nM = (q_len + BMQ - 1) / BMQ;
-  const int m_begin = CAUSAL ? min(k0 / BMQ, nM) : 0;   // queries before k0 see none of these keys
-  const int per_head = nM - m_begin;
-  const int nsteps = p.group * per_head;
-
-  const TileCopy<D, BMQ, 4> cp(wave, lane, qs);
-  const TileReads<D> rd(lane);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
-
-  auto step_coords = [&](int s, int& hq, int& q0) {
-    const int hg = s / per_head;
-    hq = hkv * p.group + hg;
-    q0 = (m_begin + s % per_head) * BMQ;
-  };
-  auto issue = [&](int s) {
-    int hq, q0;
-    step_coords(s, hq, q0);
-    char* st = smem + (s & 1) * STAGE;
-    const long long off = (q_tok0 + q0) * qs + hq * D;
-    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
-    const T* qb = (const T*)p.q + off;
-    const T* gb = (const T*)p.dout + off;
-    constexpr int L = TileCopy<D, BMQ, 4>::LOADS;
-    copy_rows_to_lds<L>(qb, bytes, st + 0 * QT + wave * L * 1024, cp.k);
-    copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
-    copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
-    copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
-    if (!VARLEN && wave == 0) {
-      // 32 (lse2, delta) pairs = 16 lanes x 16 bytes (the array is padded to
-      // 32 rows per head, so no 16-byte read straddles its end); the other
-      // lanes' offsets are out of range and write zeros past the pairs
-      const float2* sb = p.stats + ((long long)b * p.Hq + hq) * p.Sq_pad + q0;
-      copy_row_to_lds(sb, (uint32_t)(p.Sq_pad - q0) * 8u, st + 4 * QT, lane < 16 ? (uint32_t)lane * 16u : 0x40000000u);
-    }
-  };
-
-  const float c = p.scale_log2;
-  if (nsteps > 0) issue(0);
-  for (int s = 0; s < nsteps; ++s) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + 1 < nsteps) issue(s + 1);
-    int hq, q0;
-    step_coords(s, hq, q0);
-    const char* st = smem + (s & 1) * STAGE;
-    const uint32_t stl = lds0 + (s & 1) * STAGE;
-
-    // S = Q K^T and dP = dO V^T: row m of the MFMA is query key_perm(m)
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KT; ++kk) {
-      const vec8 qa = *(const vec8*)(st + 0 * QT + rd.koff(kk));
-      const vec8 ga = *(const vec8*)(st + 2 * QT + rd.koff(kk));
-      sacc = Mma<T>::run(qa, kf[kk], sacc);
-      pacc = Mma<T>::run(ga, vf[kk], pacc);
-    }
-    // register r = 4 g + i holds query 16 (g >> 1) + 8 h + 4 (g & 1) + i:
-    // 4 consecutive queries per g, read as 2 x 16 bytes of (lse2, delta)
-    // (varlen: from global memory, rows past the sequence clamped to its last
-    // row -- their Q and dO are zero, so they contribute nothing)
-    const float* sp = (const float*)(st + 4 * QT);
-    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;   // varlen layout [Hq, T]
-    vec8 pv[2], dsv[2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qr = 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-      float l2[4], dl[4];
-      if constexpr (VARLEN) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float2 v2 = sg[min(q0 + qr + i, q_len - 1)];
-          l2[i] = v2.x;
-          dl[i] = v2.y;
-        }
-      } else {
-        const float4 s01 = *(const float4*)(sp + 2 * qr);
-        const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
-        l2[0] = s01.x; l2[1] = s01.z; l2[2] = s23.x; l2[3] = s23.z;
-        dl[0] = s01.y; dl[1] = s01.w; dl[2] = s23.y; dl[3] = s23.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        const int qrow = q0 + qr + i;
-        const bool dead = (key >= k_len) || (CAUSAL && key > qrow);
-        const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2[i]));
-        const float ds = pr * (pacc[r] - dl[i]);
-        pv[g >> 1][4 * (g & 1) + i] = (T)pr;
-        dsv[g >> 1][4 * (g & 1) + i] = (T)ds;
-      }
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS (k = 16 queries per step); the eight
-    // transposed reads of block db + 1 are in flight during block db's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    i16x4 tr[2][8];
-    tr_issue8<D>(stl + 3 * QT + rd.voff(0), stl + 1 * QT + rd.voff(0), tr[0]);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      i16x4 (&cur)[8] = tr[db & 1];
-      if (db + 1 < DB) {
-        tr_issue8<D>(stl + 3 * QT + rd.voff(db + 1), stl + 1 * QT + rd.voff(db + 1), tr[(db + 1) & 1]);
-        lds_wait<14>(cur);
-        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), pv[0], dv[db]);
-        lds_wait<12>(cur);
-        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), pv[1], dv[db]);
-        lds_wait<10>(cur);
-        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[0], dk[db]);
-        lds_wait<8>(cur);
-        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[1], dk[db]);
-      } else {
-        lds_wait<6>(cur);
-        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 0), pv[0], dv[db]);
-        lds_wait<4>(cur);
-        dv[db] = Mma<T>::run(tr_pair<vec8>(cur, 1), pv[1], dv[db]);
-        lds_wait<2>(cur);
-        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 2), dsv[0], dk[db]);
-        lds_wait<0>(cur);
-        dk[db] = Mma<T>::run(tr_pair<vec8>(cur, 3), dsv[1], dk[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // dK^T, dV^T: lane holds key `key` and channels 32 db + 8 g + 4 h + 0..3
-  if (key < k_len) {
-    const long long row = (k_tok0 + key) * p.Hkv + hkv;
-    T* dkr = (T*)p.dk + row * D;
-    T* dvr = (T*)p.dv + row * D;
-    typedef T T4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        T4 wk, wv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = (T)(dk[db][4 * g + e] * p.scale);
-          wv[e] = (T)dv[db][4 * g + e];
-        }
-        *(T4*)(dkr + 32 * db + 8 * g + 4 * h) = wk;
-        *(T4*)(dvr + 32 * db + 8 * g + 4 * h) = wv;
-      }
-  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -612,16 +326,11 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int lds_kv = 2 * (4 * 32 * 2 * D + 1024);
   constexpr int lds_q = 3 * (3 * 64 * 2 * D);
-  static const hipError_t a1 = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
   static const hipError_t a2 = hipFuncSetAttribute((const void*)bwd_dq_kernel<T, D, CAUSAL, VARLEN>,
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_q);
-  if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds_kv, s, p);
-  e = hipGetLastError();
+  e = launch_bwd_dkdv(p, std::is_same<T, __bf16>::value ? 0 : 1, D, CAUSAL, VARLEN, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dq), dim3(256), lds_q, s, p);
   return hipGetLastError();

@@ -1,0 +1,390 @@
+// attn_bwd_dkdv.hip -- dK and dV of the attention backward (bf16 / fp16,
+// d in {64, 128}, dense or varlen, causal or not, GQA).
+//
+// Gradient math (Hopper tag page, contents 7.1): with P recomputed from the
+// forward's LSE, dV = P^T dO and dK = scale dS^T Q, dS = P (dP - delta),
+// dP = dO V^T.
+//
+// Workgroup = (batch, KV head, 128 keys) -- varlen: (KV head, sequence, key
+// block), found by a scan of the offsets -- in ascending key-block order (the
+// first blocks see the most queries under a causal mask: longest first).
+// Each of the 4 waves owns 32 keys and walks 32-query steps of every query
+// head of the KV group (GQA sums in registers, no atomics):
+//   S = Q K^T, dP = dO V^T   (query rows x keys; the rows are permuted by
+//                             key_perm so each accumulator, 8 registers at a
+//                             time, is the B operand of the next MFMAs)
+//   P = exp2(c S - lse2), dS = P (dP - delta)          (vector units)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A operands by ds_read_b64_tr_b16)
+//
+// Registers are assigned by name, as in the forward's wide kernel: the dK^T
+// and dV^T accumulators and the wave's K and V fragments (the B operands of
+// the first two GEMMs) live in fixed AGPRs and every MFMA is inline assembly
+// that names them; S and dP are written straight to VGPRs, where the vector
+// code reads them.  Left to itself the compiler placed S and dP in AGPRs and
+// copied them out (and zeroed them) on every step.  The build checks that the
+// compiler uses no AGPR in this file and spills nothing.
+//
+// AGPR map (DB = D / 32 channel blocks, KT = D / 16 k-steps):
+//   a[0 : 16 DB)              dV^T, block db at 16 db
+//   a[16 DB : 32 DB)          dK^T, block db at 16 DB + 16 db
+//   a[32 DB : 32 DB + 4 KT)   K fragments, k-step kk at 32 DB + 4 kk
+//   a[... : + 4 KT)           V fragments
+// Hazards the compiler cannot see are kept by the order of the statements:
+// S and dP are read after an s_nop run behind their last MFMA; each dV/dK
+// MFMA has another MFMA between it and the next one on the same block; the
+// accumulators are read after an s_nop run.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "bwd_common.h"
+#include "kernel_common.h"
+#include "kernels.h"
+#include "wide_regs.h"
+
+namespace attn {
+namespace dkdv {
+
+using wide::Asm;
+
+template <int D>
+struct Map {
+  static constexpr int DB = D / 32, KT = D / 16;
+  static constexpr int DV = 0, DK = 16 * DB, KF = 32 * DB, VF = 32 * DB + 4 * KT;
+};
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
+// fragment (K or V) k-step kk -> its four AGPRs
+template <int BASE, int KK>
+constexpr Asm frag_load_text() {
+  Asm t;
+  t.s("global_load_dwordx4 ").a(BASE + 4 * KK, 4).s(", %0, off");
+  return t;
+}
+template <int BASE, int KK>
+__device__ __forceinline__ void frag_load(const void* ptr) {
+  asm volatile((frag_load_text<BASE, KK>())::"v"(ptr) : "memory");
+}
+
+// accumulators a[0 : 32 DB) = 0.  The clobber list reserves the AGPRs the
+// map uses (the compiler does not read the assembly text): all 256 for
+// d = 128, a0..a95 for d = 64, which leaves room for two waves per SIMD.
+#define DKDV_CLOBBER_AGPRS_96                                                                            \
+  "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", ATTN_AGPRS_10(1), ATTN_AGPRS_10(2),         \
+      ATTN_AGPRS_10(3), ATTN_AGPRS_10(4), ATTN_AGPRS_10(5), ATTN_AGPRS_10(6), ATTN_AGPRS_10(7), ATTN_AGPRS_10(8), \
+      "a90", "a91", "a92", "a93", "a94", "a95"
+static_assert(Map<64>::VF + 4 * Map<64>::KT == 96, "d = 64 register map");
+static_assert(Map<128>::VF + 4 * Map<128>::KT <= 256, "d = 128 register map");
+
+template <int D>
+constexpr Asm zero_text() {
+  Asm t;
+  for (int r = 0; r < 32 * Map<D>::DB; ++r) t.s("v_accvgpr_write_b32 a").i(r).s(", 0\n\t");
+  return t;
+}
+template <int D>
+__device__ __forceinline__ void acc_zero() {
+  if constexpr (D == 64) asm volatile((zero_text<D>())::: DKDV_CLOBBER_AGPRS_96);
+  else asm volatile((zero_text<D>())::: ATTN_CLOBBER_AGPRS);
+}
+
+// S or dP (VGPRs) = / += row operand (VGPR) x fragment k-step kk (AGPR)
+template <typename T, int BASE, int KK, bool FIRST>
+constexpr Asm first_text() {
+  Asm t;
+  t.s(wide::mfma_name<T>()).s("%0, %1, ").a(BASE + 4 * KK, 4).s(FIRST ? ", 0" : ", %0");
+  return t;
+}
+template <typename T, int BASE, int KK, bool FIRST, typename V8>
+__device__ __forceinline__ void mfma_first(f32x16& acc, const V8& a) {
+  if constexpr (FIRST) asm volatile((first_text<T, BASE, KK, true>()) : "=v"(acc) : "v"(a));
+  else asm volatile((first_text<T, BASE, KK, false>()) : "+v"(acc) : "v"(a));
+}
+
+// accumulator block at AGPR ACC += A (VGPR) x B (VGPR)
+template <typename T, int ACC>
+constexpr Asm acc_text() {
+  Asm t;
+  t.s(wide::mfma_name<T>()).a(ACC, 16).s(", %0, %1, ").a(ACC, 16);
+  return t;
+}
+template <typename T, int ACC, typename V8>
+__device__ __forceinline__ void mfma_acc(const V8& a, const V8& b) {
+  asm volatile((acc_text<T, ACC>())::"v"(a), "v"(b));
+}
+
+// s_nop run after MFMAs before their results are read by vector code
+__device__ __forceinline__ void pad2(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
+template <int ACC>
+constexpr Asm read_text() {
+  Asm t;
+  for (int e = 0; e < 16; ++e) {
+    t.s("v_accvgpr_read_b32 %").i(e).s(", a").i(ACC + e);
+    if (e < 15) t.s("\n\t");
+  }
+  return t;
+}
+template <int ACC>
+__device__ __forceinline__ f32x16 acc_read() {
+  float x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15;
+  asm volatile((read_text<ACC>())
+               : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7), "=v"(x8),
+                 "=v"(x9), "=v"(x10), "=v"(x11), "=v"(x12), "=v"(x13), "=v"(x14), "=v"(x15));
+  return f32x16{x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15};
+}
+
+}  // namespace dkdv
+
+// VARLEN: p.B sequences packed along the token axis (cu_seqlens); the
+// statistics are then read from global memory (their per-sequence rows are
+// not 16-byte aligned for the copy).
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+bwd_dkdv_kernel(BwdParams p) {
+  using namespace dkdv;
+  typedef typename Mma<T>::vec8 vec8;
+  using M = Map<D>;
+  constexpr int BMQ = 32;                 // query rows per step
+  constexpr int KT = M::KT;
+  constexpr int DB = M::DB;
+  constexpr int ROW = 2 * D;
+  constexpr int QT = BMQ * ROW;           // one 32-row tile
+  constexpr int STAT = 1024;              // (lse2, delta) of 32 rows, in a 1 KiB slot
+  // stage: [Q row-swizzled | Q transposed-swizzled | dO row | dO transposed | stats]
+  constexpr int STAGE = 4 * QT + STAT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hkv, nblk, q_len, k_len;
+  long long q_tok0, k_tok0;               // token index of the sequence's first query / key
+  if constexpr (VARLEN) {
+    hkv = blockIdx.x % p.Hkv;
+    int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
+    for (; sq < p.B; ++sq) {
+      start = p.cu_seqlens[sq];
+      len = p.cu_seqlens[sq + 1] - start;
+      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
+      if (r < nb) break;
+      r -= nb;
+    }
+    if (sq >= p.B) return;                // beyond the last block (uniform over the workgroup)
+    b = 0;
+    nblk = r;
+    q_len = k_len = len;
+    q_tok0 = k_tok0 = start;
+  } else {
+    const int G = p.B * p.Hkv;
+    nblk = blockIdx.x / G;
+    const int gi = blockIdx.x % G;
+    b = gi / p.Hkv;
+    hkv = gi % p.Hkv;
+    q_len = p.Sq;
+    k_len = p.Sk;
+    q_tok0 = (long long)b * p.Sq;
+    k_tok0 = (long long)b * p.Sk;
+  }
+  const int k0 = nblk * kBwdBlockN;
+  const int key = k0 + wave * 32 + l32;   // this lane's key (column of S), sequence position
+  const int qs = p.Hq * D;                // token stride of q, o, dO, dQ
+
+  acc_zero<D>();
+  // K and V of the lane's key (B operands, k = head dimension) into their
+  // AGPRs; rows past the end read a valid row and are masked
+  {
+    const long long row = (k_tok0 + min(key, k_len - 1)) * p.Hkv + hkv;
+    const T* kr = (const T*)p.k + row * D + 8 * h;
+    const T* vr = (const T*)p.v + row * D + 8 * h;
+    static_for<KT>([&](auto kk) {
+      frag_load<M::KF, decltype(kk)::value>(kr + 16 * kk);
+      frag_load<M::VF, decltype(kk)::value>(vr + 16 * kk);
+    });
+  }
+
+  const int nM = (q_len + BMQ - 1) / BMQ;
+  const int m_begin = CAUSAL ? min(k0 / BMQ, nM) : 0;   // queries before k0 see none of these keys
+  const int per_head = nM - m_begin;
+  const int nsteps = p.group * per_head;
+
+  const TileCopy<D, BMQ, 4> cp(wave, lane, qs);
+  const TileReads<D> rd(lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+
+  auto step_coords = [&](int s, int& hq, int& q0) {
+    const int hg = s / per_head;
+    hq = hkv * p.group + hg;
+    q0 = (m_begin + s % per_head) * BMQ;
+  };
+  auto issue = [&](int s) {
+    int hq, q0;
+    step_coords(s, hq, q0);
+    char* st = smem + (s & 1) * STAGE;
+    const long long off = (q_tok0 + q0) * qs + hq * D;
+    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
+    const T* qb = (const T*)p.q + off;
+    const T* gb = (const T*)p.dout + off;
+    constexpr int L = TileCopy<D, BMQ, 4>::LOADS;
+    copy_rows_to_lds<L>(qb, bytes, st + 0 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
+    copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
+    if (!VARLEN && wave == 0) {
+      // 32 (lse2, delta) pairs = 16 lanes x 16 bytes (the array is padded to
+      // 32 rows per head, so no 16-byte read straddles its end); the other
+      // lanes' offsets are out of range and write zeros past the pairs
+      const float2* sb = p.stats + ((long long)b * p.Hq + hq) * p.Sq_pad + q0;
+      copy_row_to_lds(sb, (uint32_t)(p.Sq_pad - q0) * 8u, st + 4 * QT, lane < 16 ? (uint32_t)lane * 16u : 0x40000000u);
+    }
+  };
+
+  const float c = p.scale_log2;
+  if (nsteps > 0) issue(0);
+  for (int s = 0; s < nsteps; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 1 < nsteps) issue(s + 1);
+    int hq, q0;
+    step_coords(s, hq, q0);
+    const char* st = smem + (s & 1) * STAGE;
+    const uint32_t stl = lds0 + (s & 1) * STAGE;
+
+    // S = Q K^T and dP = dO V^T: row m of the MFMA is query key_perm(m)
+    f32x16 sacc, pacc;
+    static_for<KT>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      const vec8 qa = *(const vec8*)(st + 0 * QT + rd.koff(kk));
+      const vec8 ga = *(const vec8*)(st + 2 * QT + rd.koff(kk));
+      mfma_first<T, M::KF, kk, kk == 0>(sacc, qa);
+      mfma_first<T, M::VF, kk, kk == 0>(pacc, ga);
+    });
+    pad2(sacc, pacc);
+    // register r = 4 g + i holds query 16 (g >> 1) + 8 h + 4 (g & 1) + i:
+    // 4 consecutive queries per g, read as 2 x 16 bytes of (lse2, delta)
+    // (varlen: from global memory, rows past the sequence clamped to its last
+    // row -- their Q and dO are zero, so they contribute nothing)
+    const float* sp = (const float*)(st + 4 * QT);
+    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;   // varlen layout [Hq, T]
+    vec8 pv[2], dsv[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qr = 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+      float l2[4], dl[4];
+      if constexpr (VARLEN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 v2 = sg[min(q0 + qr + i, q_len - 1)];
+          l2[i] = v2.x;
+          dl[i] = v2.y;
+        }
+      } else {
+        const float4 s01 = *(const float4*)(sp + 2 * qr);
+        const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
+        l2[0] = s01.x; l2[1] = s01.z; l2[2] = s23.x; l2[3] = s23.z;
+        dl[0] = s01.y; dl[1] = s01.w; dl[2] = s23.y; dl[3] = s23.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const int qrow = q0 + qr + i;
+        const bool dead = (key >= k_len) || (CAUSAL && key > qrow);
+        const float pr = dead ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2[i]));
+        const float ds = pr * (pacc[r] - dl[i]);
+        pv[g >> 1][4 * (g & 1) + i] = (T)pr;
+        dsv[g >> 1][4 * (g & 1) + i] = (T)ds;
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (k = 16 queries per step); the eight
+    // transposed reads of block db + 1 are in flight during block db's MFMAs.
+    // Read pairs 0, 1 are dO^T, 2, 3 are Q^T; waiting for pair 2 covers 1.
+    __builtin_amdgcn_sched_barrier(0);
+    i16x4 tr[2][8];
+    tr_issue8<D>(stl + 3 * QT + rd.voff(0), stl + 1 * QT + rd.voff(0), tr[0]);
+    static_for<DB>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      i16x4(&cur)[8] = tr[db & 1];
+      constexpr int DVB = M::DV + 16 * db, DKB = M::DK + 16 * db;
+      if constexpr (db + 1 < DB) {
+        tr_issue8<D>(stl + 3 * QT + rd.voff(db + 1), stl + 1 * QT + rd.voff(db + 1), tr[(db + 1) & 1]);
+        lds_wait<14>(cur);
+        mfma_acc<T, DVB>(tr_pair<vec8>(cur, 0), pv[0]);
+        lds_wait<10>(cur);
+        mfma_acc<T, DKB>(tr_pair<vec8>(cur, 2), dsv[0]);
+        mfma_acc<T, DVB>(tr_pair<vec8>(cur, 1), pv[1]);
+        lds_wait<8>(cur);
+        mfma_acc<T, DKB>(tr_pair<vec8>(cur, 3), dsv[1]);
+      } else {
+        lds_wait<6>(cur);
+        mfma_acc<T, DVB>(tr_pair<vec8>(cur, 0), pv[0]);
+        lds_wait<2>(cur);
+        mfma_acc<T, DKB>(tr_pair<vec8>(cur, 2), dsv[0]);
+        mfma_acc<T, DVB>(tr_pair<vec8>(cur, 1), pv[1]);
+        lds_wait<0>(cur);
+        mfma_acc<T, DKB>(tr_pair<vec8>(cur, 3), dsv[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // dK^T, dV^T: lane holds key `key` and channels 32 db + 8 g + 4 h + 0..3
+  wide::acc_read_pad();
+  if (key < k_len) {
+    const long long row = (k_tok0 + key) * p.Hkv + hkv;
+    T* dkr = (T*)p.dk + row * D;
+    T* dvr = (T*)p.dv + row * D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    static_for<DB>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      const f32x16 dkx = acc_read<M::DK + 16 * db>();
+      const f32x16 dvx = acc_read<M::DV + 16 * db>();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (T)(dkx[4 * g + e] * p.scale);
+          wv[e] = (T)dvx[4 * g + e];
+        }
+        *(T4*)(dkr + 32 * db + 8 * g + 4 * h) = wk;
+        *(T4*)(dvr + 32 * db + 8 * g + 4 * h) = wv;
+      }
+    });
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
+  constexpr int lds = 2 * (4 * 32 * 2 * D + 1024);
+  static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dkdv_v(const BwdParams& p, int causal, int varlen, hipStream_t s) {
+  if (varlen) return causal ? launch_dkdv_t<T, D, true, true>(p, s) : launch_dkdv_t<T, D, false, true>(p, s);
+  return causal ? launch_dkdv_t<T, D, true, false>(p, s) : launch_dkdv_t<T, D, false, false>(p, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (dtype == 0)
+    return d == 128 ? launch_dkdv_v<__bf16, 128>(p, causal, varlen, s) : launch_dkdv_v<__bf16, 64>(p, causal, varlen, s);
+  return d == 128 ? launch_dkdv_v<_Float16, 128>(p, causal, varlen, s) : launch_dkdv_v<_Float16, 64>(p, causal, varlen, s);
+}
+
+}  // namespace attn
