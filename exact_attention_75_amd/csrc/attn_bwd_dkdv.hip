@@ -105,7 +105,7 @@ constexpr Asm first_text() {
 }
 template <typename T, int BASE, int KK, bool FIRST, typename V8>
 __device__ __forceinline__ void mfma_first(f32x16& acc, const V8& a) {
-  if constexpr (FIRST) asm volatile((first_text<T, BASE, KK, true>()) : "=v"(acc) : "v"(a));
+  if constexpr (FIRST) asm volatile((first_text<T, BASE, KK, true>()) : "=&v"(acc) : "v"(a));
   else asm volatile((first_text<T, BASE, KK, false>()) : "+v"(acc) : "v"(a));
 }
 
@@ -365,13 +365,379 @@ bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------- pipelined
+// The same work per step as bwd_dkdv_kernel, reordered so that the vector
+// work of step s (P and dS from S_s, dP_s) runs under MFMAs: query rows 0-15
+// of the step under dV/dK of step s - 1, rows 16-31 under S, dP of step s + 1.
+// LDS ring of four stages; in iteration s, stage s - 1 feeds the transposed
+// reads of dV/dK(s - 1), stage s + 1 the row reads of S, dP(s + 1) and the
+// statistics of step s + 1, and stage s + 2 is being copied (the barrier at
+// the top of iteration s frees it: every wave has finished iteration s - 1).
+// LDS reads are inline assembly waited for with explicit lgkmcnt values
+// (reads complete in order); the vector code is pinned between MFMAs with
+// scheduling barriers.
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_pipe_kernel(BwdParams p) {
+  using namespace dkdv;
+  typedef typename Mma<T>::vec8 vec8;
+  using M = Map<D>;
+  constexpr int BMQ = 32;                 // query rows per step
+  constexpr int KT = M::KT;
+  constexpr int DB = M::DB;
+  constexpr int ROW = 2 * D;
+  constexpr int QT = BMQ * ROW;
+  constexpr int STAT = 1024;
+  // stage: [Q row-swizzled | Q transposed-swizzled | dO row | dO transposed | stats]
+  constexpr int STAGE = 4 * QT + STAT;
+  constexpr int HEAD = KT < 4 ? KT : 4;   // row-read batches in flight in S, dP
+  static_assert(KT % 4 == 0 && 4 % DB == 0 || DB % 4 == 0, "vector work placement");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hkv, nblk, q_len, k_len;
+  long long q_tok0, k_tok0;
+  if constexpr (VARLEN) {
+    hkv = blockIdx.x % p.Hkv;
+    int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
+    for (; sq < p.B; ++sq) {
+      start = p.cu_seqlens[sq];
+      len = p.cu_seqlens[sq + 1] - start;
+      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
+      if (r < nb) break;
+      r -= nb;
+    }
+    if (sq >= p.B) return;
+    b = 0;
+    nblk = r;
+    q_len = k_len = len;
+    q_tok0 = k_tok0 = start;
+  } else {
+    const int G = p.B * p.Hkv;
+    nblk = blockIdx.x / G;
+    const int gi = blockIdx.x % G;
+    b = gi / p.Hkv;
+    hkv = gi % p.Hkv;
+    q_len = p.Sq;
+    k_len = p.Sk;
+    q_tok0 = (long long)b * p.Sq;
+    k_tok0 = (long long)b * p.Sk;
+  }
+  const int k0 = nblk * kBwdBlockN;
+  const int key = k0 + wave * 32 + l32;
+  const int qs = p.Hq * D;
+
+  acc_zero<D>();
+  {
+    const long long row = (k_tok0 + min(key, k_len - 1)) * p.Hkv + hkv;
+    const T* kr = (const T*)p.k + row * D + 8 * h;
+    const T* vr = (const T*)p.v + row * D + 8 * h;
+    static_for<KT>([&](auto kk) {
+      frag_load<M::KF, decltype(kk)::value>(kr + 16 * kk);
+      frag_load<M::VF, decltype(kk)::value>(vr + 16 * kk);
+    });
+  }
+
+  const int nM = (q_len + BMQ - 1) / BMQ;
+  const int m_begin = CAUSAL ? min(k0 / BMQ, nM) : 0;
+  const int per_head = nM - m_begin;
+  const int nsteps = p.group * per_head;
+
+  const TileCopy<D, BMQ, 4> cp(wave, lane, qs);
+  const TileReads<D> rd(lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
+  auto stage = [&](int s) { return lds0 + (uint32_t)(s & 3) * STAGE; };
+
+  auto step_coords = [&](int s, int& hq, int& q0) {
+    const int hg = s / per_head;
+    hq = hkv * p.group + hg;
+    q0 = (m_begin + s % per_head) * BMQ;
+  };
+  auto issue = [&](int s) {
+    int hq, q0;
+    step_coords(s, hq, q0);
+    char* st = smem + (s & 3) * STAGE;
+    const long long off = (q_tok0 + q0) * qs + hq * D;
+    const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
+    const T* qb = (const T*)p.q + off;
+    const T* gb = (const T*)p.dout + off;
+    constexpr int L = TileCopy<D, BMQ, 4>::LOADS;
+    copy_rows_to_lds<L>(qb, bytes, st + 0 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
+    copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
+    copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
+    if (!VARLEN && wave == 0) {
+      const float2* sb = p.stats + ((long long)b * p.Hq + hq) * p.Sq_pad + q0;
+      copy_row_to_lds(sb, (uint32_t)(p.Sq_pad - q0) * 8u, st + 4 * QT, lane < 16 ? (uint32_t)lane * 16u : 0x40000000u);
+    }
+  };
+
+  // statistics of a step: st[2 g + j] = (lse2, delta) of query rows
+  // qr + 2 j and qr + 2 j + 1, qr = 16 (g >> 1) + 8 h + 4 (g & 1)
+  auto stats_lds = [&](uint32_t sb, float4 (&st)[8]) {
+    const uint32_t a = sb + 4 * QT + 64 * h;
+    i32x4 r[8];
+    r[0] = lds_rd128<0>(a);
+    r[1] = lds_rd128<16>(a);
+    r[2] = lds_rd128<32>(a);
+    r[3] = lds_rd128<48>(a);
+    r[4] = lds_rd128<128>(a);
+    r[5] = lds_rd128<144>(a);
+    r[6] = lds_rd128<160>(a);
+    r[7] = lds_rd128<176>(a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st[j] = __builtin_bit_cast(float4, r[j]);
+  };
+  // varlen: from global memory ([Hq, T]); rows past the sequence read its
+  // last row (their Q and dO are zero, so they contribute nothing)
+  auto stats_glb = [&](int s, float4 (&st)[8]) {
+    int hq, q0;
+    step_coords(s, hq, q0);
+    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = q0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + 2 * j;
+        const float2 x = sg[min(r, q_len - 1)];
+        const float2 y = sg[min(r + 1, q_len - 1)];
+        st[2 * g + j] = make_float4(x.x, x.y, y.x, y.y);
+      }
+  };
+
+  const float c = p.scale_log2;
+  // element (g, i) of a step at q0 is masked iff tl - q0 > 16 (g >> 1) + 4 (g & 1) + i
+  // (causal: the key is past the query row; any: the key is past the end)
+  constexpr int BIG = 1 << 30;
+  const int tl = key >= k_len ? BIG : (CAUSAL ? key - 8 * h : -BIG);
+
+  // P and dS of elements E, E + 1 (E even; register r = 4 g + i holds query
+  // row 16 (g >> 1) + 8 h + 4 (g & 1) + i) into the 16-bit B operands
+  auto pair = [&](auto ec, const f32x16& sc, const f32x16& pc, const float4 (&st)[8], int t, vec8 (&pvc)[2],
+                  vec8 (&dsc)[2]) {
+    constexpr int E = decltype(ec)::value;
+    constexpr int g = E >> 2, i = E & 3;
+    constexpr int cr = 16 * (g >> 1) + 4 * (g & 1) + i;
+    const float4 sv = st[2 * g + (i >> 1)];
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E], c, -sv.x));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E + 1], c, -sv.z));
+    p0 = t > cr ? 0.f : p0;
+    p1 = t > cr + 1 ? 0.f : p1;
+    const float d0 = p0 * (pc[E] - sv.y);
+    const float d1 = p1 * (pc[E + 1] - sv.w);
+    constexpr int v = g >> 1, o = 4 * (g & 1) + i;
+    typedef T T2 __attribute__((ext_vector_type(2)));
+    const T2 pp = {(T)p0, (T)p1};
+    const T2 dd = {(T)d0, (T)d1};
+    // pinned here: otherwise the compiler sinks the whole computation to the
+    // first use (the next iteration's MFMAs), undoing the interleave
+    keep_vec(pp);
+    keep_vec(dd);
+    pvc[v][o] = pp[0];
+    pvc[v][o + 1] = pp[1];
+    dsc[v][o] = dd[0];
+    dsc[v][o + 1] = dd[1];
+  };
+
+  // row reads of S, dP: batch kk = (Q, dO) 16 bytes each at the lane's offset
+  auto rowread = [&](auto kkc, uint32_t sb, i32x4 (&qg)[KT][2]) {
+    constexpr int kk = decltype(kkc)::value;
+    const uint32_t a = sb + (uint32_t)rd.koff(kk);
+    qg[kk][0] = lds_rd128<0>(a);
+    qg[kk][1] = lds_rd128<2 * QT>(a);
+  };
+  auto rowread_head = [&](uint32_t sb, i32x4 (&qg)[KT][2]) {
+    static_for<HEAD>([&](auto kk) { rowread(kk, sb, qg); });
+  };
+
+  // S = Q K^T, dP = dO V^T of the step in stage sb (its first HEAD batches
+  // already issued); HOOK(kk) runs after k-step kk's MFMAs
+  auto sdp = [&](uint32_t sb, f32x16& sn, f32x16& pn, i32x4 (&qg)[KT][2], auto&& hook) {
+    static_for<KT>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      constexpr int after = (KT - 1 - kk) < (HEAD - 1) ? (KT - 1 - kk) : (HEAD - 1);
+      lds_wait<2 * after>(qg[kk]);
+      mfma_first<T, M::KF, kk, kk == 0>(sn, __builtin_bit_cast(vec8, qg[kk][0]));
+      mfma_first<T, M::VF, kk, kk == 0>(pn, __builtin_bit_cast(vec8, qg[kk][1]));
+      if constexpr (kk + HEAD < KT) rowread(std::integral_constant<int, kk + HEAD>{}, sb, qg);
+      hook(kkc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // dV^T += dO^T P, dK^T += Q^T dS of the step in stage sb; with HEAD_NEXT the
+  // first row reads of the next step (stage sbn) are issued during the last
+  // channel block; HOOK(m) runs after MFMA m (4 per channel block)
+  auto dvdk = [&](auto nextc, uint32_t sb, uint32_t sbn, const vec8 (&pvp)[2], const vec8 (&dsp)[2],
+                  i32x4 (&qg)[KT][2], auto&& hook) {
+    constexpr bool NEXT = decltype(nextc)::value;
+    const uint32_t a = sb + QT + rd.voff0;
+    i16x4 tr[2][8];
+    auto tr_issue = [&](auto dbc, i16x4(&r)[8]) {
+      constexpr int db = decltype(dbc)::value;
+      constexpr int R = ROW;
+      const uint32_t x = sb + QT + (rd.voff0 ^ (uint32_t)(db << 6));
+      r[0] = lds_tr16<2 * QT>(x);
+      r[1] = lds_tr16<2 * QT + 4 * R>(x);
+      r[2] = lds_tr16<2 * QT + 16 * R>(x);
+      r[3] = lds_tr16<2 * QT + 20 * R>(x);
+      r[4] = lds_tr16<0>(x);
+      r[5] = lds_tr16<4 * R>(x);
+      r[6] = lds_tr16<16 * R>(x);
+      r[7] = lds_tr16<20 * R>(x);
+    };
+    (void)a;
+    tr_issue(std::integral_constant<int, 0>{}, tr[0]);
+    static_for<DB>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      i16x4(&cur)[8] = tr[db & 1];
+      constexpr int DVB = M::DV + 16 * db, DKB = M::DK + 16 * db;
+      constexpr int nb = (db + 1 < DB) ? 8 : (NEXT ? 2 * HEAD : 0);
+      if constexpr (db + 1 < DB) tr_issue(std::integral_constant<int, db + 1>{}, tr[(db + 1) & 1]);
+      else if constexpr (NEXT) rowread_head(sbn, qg);
+      lds_wait<6 + nb>(cur);
+      mfma_acc<T, DVB>(tr_pair<vec8>(cur, 0), pvp[0]);
+      hook(std::integral_constant<int, 4 * db + 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait<2 + nb>(cur);
+      mfma_acc<T, DKB>(tr_pair<vec8>(cur, 2), dsp[0]);
+      hook(std::integral_constant<int, 4 * db + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc<T, DVB>(tr_pair<vec8>(cur, 1), pvp[1]);
+      hook(std::integral_constant<int, 4 * db + 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait<0 + nb>(cur);
+      mfma_acc<T, DKB>(tr_pair<vec8>(cur, 3), dsp[1]);
+      hook(std::integral_constant<int, 4 * db + 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto no_hook = [](auto) {};
+
+  // one iteration: P, dS of step s (from sc, pc, stc) into pvc, dsc, under
+  // dV/dK of step s - 1 (pvp, dsp) and S, dP of step s + 1 (into sn, pn)
+  auto body = [&](auto prevc, auto nextc, int s, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
+                  const vec8 (&pvp)[2], const vec8 (&dsp)[2], vec8 (&pvc)[2], vec8 (&dsc)[2],
+                  const float4 (&stc)[8], float4 (&stn)[8]) {
+    constexpr bool PREV = decltype(prevc)::value, NEXT = decltype(nextc)::value;
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (VARLEN && NEXT) stats_glb(s + 1, stn);
+    if (s + 2 < nsteps) issue(s + 2);
+    const uint32_t sbn = stage(s + 1);
+    if constexpr (!VARLEN && NEXT) stats_lds(sbn, stn);
+    int hq, q0;
+    step_coords(s, hq, q0);
+    const int t = tl - q0;
+    i32x4 qg[KT][2];
+    __builtin_amdgcn_sched_barrier(0);
+    // rows 0-15: pairs 0..3
+    auto hook1 = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr ((m + 1) % DB == 0) pair(std::integral_constant<int, 2 * ((m + 1) / DB - 1)>{}, sc, pc, stc, t, pvc, dsc);
+    };
+    if constexpr (PREV) {
+      dvdk(nextc, stage(s - 1), sbn, pvp, dsp, qg, hook1);
+    } else {
+      if constexpr (NEXT) rowread_head(sbn, qg);
+      static_for<4>([&](auto e) { pair(std::integral_constant<int, 2 * decltype(e)::value>{}, sc, pc, stc, t, pvc, dsc); });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // rows 16-31: pairs 4..7
+    if constexpr (NEXT) {
+      sdp(sbn, sn, pn, qg, [&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        constexpr int per = KT / 4;
+        if constexpr ((kk + 1) % per == 0) pair(std::integral_constant<int, 8 + 2 * ((kk + 1) / per - 1)>{}, sc, pc, stc, t, pvc, dsc);
+      });
+      pad2(sn, pn);
+    } else {
+      static_for<4>([&](auto e) { pair(std::integral_constant<int, 8 + 2 * decltype(e)::value>{}, sc, pc, stc, t, pvc, dsc); });
+    }
+  };
+
+  const std::integral_constant<bool, true> yes;
+  const std::integral_constant<bool, false> no;
+  f32x16 sa, pa, sb2, pb2;
+  vec8 px[2], dx[2], py[2], dy[2];
+  float4 sta[8], stb[8];
+  i32x4 qg0[KT][2];
+  if (nsteps > 0) {
+    issue(0);
+    if (nsteps > 1) issue(1);
+    if constexpr (VARLEN) stats_glb(0, sta);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (!VARLEN) stats_lds(stage(0), sta);
+    rowread_head(stage(0), qg0);
+    sdp(stage(0), sa, pa, qg0, no_hook);
+    pad2(sa, pa);
+    // step s consumes S set s % 2 (a, b), produces P set s % 2 (x, y) and
+    // statistics set (s + 1) % 2
+    if (nsteps == 1) {
+      body(no, no, 0, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+      dvdk(no, stage(0), 0, px, dx, qg0, no_hook);
+    } else {
+      body(no, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+      int s = 1;
+      for (; s + 2 < nsteps; s += 2) {
+        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
+        body(yes, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+      }
+      if (s + 1 < nsteps) {
+        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
+        body(yes, no, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+        dvdk(no, stage(s + 1), 0, px, dx, qg0, no_hook);
+      } else {
+        body(yes, no, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
+        dvdk(no, stage(s), 0, py, dy, qg0, no_hook);
+      }
+    }
+  }
+
+  wide::acc_read_pad();
+  if (key < k_len) {
+    const long long row = (k_tok0 + key) * p.Hkv + hkv;
+    T* dkr = (T*)p.dk + row * D;
+    T* dvr = (T*)p.dv + row * D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    static_for<DB>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      const f32x16 dkx = acc_read<M::DK + 16 * db>();
+      const f32x16 dvx = acc_read<M::DV + 16 * db>();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (T)(dkx[4 * g + e] * p.scale);
+          wv[e] = (T)dvx[4 * g + e];
+        }
+        *(T4*)(dkr + 32 * db + 8 * g + 4 * h) = wk;
+        *(T4*)(dvr + 32 * db + 8 * g + 4 * h) = wv;
+      }
+    });
+  }
+}
+
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
-  constexpr int lds = 2 * (4 * 32 * 2 * D + 1024);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
+  if constexpr (D == 128) {
+    constexpr int lds = 4 * (4 * 32 * 2 * D + 1024);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_pipe_kernel<T, D, CAUSAL, VARLEN>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
+  } else {
+    constexpr int lds = 2 * (4 * 32 * 2 * D + 1024);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
+  }
   return hipGetLastError();
 }
 
