@@ -373,10 +373,13 @@ bwd_dkdv_kernel(BwdParams p) {
 // reads of dV/dK(s - 1), stage s + 1 the row reads of S, dP(s + 1) and the
 // statistics of step s + 1, and stage s + 2 is being copied (the barrier at
 // the top of iteration s frees it: every wave has finished iteration s - 1).
-// LDS reads are inline assembly waited for with explicit lgkmcnt values
-// (reads complete in order); the vector code is pinned between MFMAs with
-// scheduling barriers.
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+// The first transposed reads of an iteration and the statistics it needs are
+// issued at the end of the one before, so the first MFMA follows the barrier
+// at once; the copy of stage s + 2 is issued after that MFMA.  LDS reads are
+// inline assembly waited for with explicit lgkmcnt values (reads complete in
+// order); the vector code is pinned between MFMAs with scheduling barriers.
+// Dense batches only (the statistics come with the LDS copies).
+template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_pipe_kernel(BwdParams p) {
   using namespace dkdv;
@@ -391,7 +394,8 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   // stage: [Q row-swizzled | Q transposed-swizzled | dO row | dO transposed | stats]
   constexpr int STAGE = 4 * QT + STAT;
   constexpr int HEAD = KT < 4 ? KT : 4;   // row-read batches in flight in S, dP
-  static_assert(KT % 4 == 0 && 4 % DB == 0 || DB % 4 == 0, "vector work placement");
+  static_assert(KT % 4 == 0 && (4 % DB == 0 || DB % 4 == 0), "vector work placement");
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -400,34 +404,13 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  int b, hkv, nblk, q_len, k_len;
-  long long q_tok0, k_tok0;
-  if constexpr (VARLEN) {
-    hkv = blockIdx.x % p.Hkv;
-    int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
-    for (; sq < p.B; ++sq) {
-      start = p.cu_seqlens[sq];
-      len = p.cu_seqlens[sq + 1] - start;
-      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
-      if (r < nb) break;
-      r -= nb;
-    }
-    if (sq >= p.B) return;
-    b = 0;
-    nblk = r;
-    q_len = k_len = len;
-    q_tok0 = k_tok0 = start;
-  } else {
-    const int G = p.B * p.Hkv;
-    nblk = blockIdx.x / G;
-    const int gi = blockIdx.x % G;
-    b = gi / p.Hkv;
-    hkv = gi % p.Hkv;
-    q_len = p.Sq;
-    k_len = p.Sk;
-    q_tok0 = (long long)b * p.Sq;
-    k_tok0 = (long long)b * p.Sk;
-  }
+  const int G = p.B * p.Hkv;
+  const int nblk = blockIdx.x / G;
+  const int b = (blockIdx.x % G) / p.Hkv;
+  const int hkv = (blockIdx.x % G) % p.Hkv;
+  const int q_len = p.Sq, k_len = p.Sk;
+  const long long q_tok0 = (long long)b * p.Sq;
+  const long long k_tok0 = (long long)b * p.Sk;
   const int k0 = nblk * kBwdBlockN;
   const int key = k0 + wave * 32 + l32;
   const int qs = p.Hq * D;
@@ -453,14 +436,20 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
   auto stage = [&](int s) { return lds0 + (uint32_t)(s & 3) * STAGE; };
 
-  auto step_coords = [&](int s, int& hq, int& q0) {
-    const int hg = s / per_head;
-    hq = hkv * p.group + hg;
-    q0 = (m_begin + s % per_head) * BMQ;
+  // step s = (query head hkv * group + hg, query block qb), advanced by one
+  // step at a time (steps walk the blocks of one head, then the next head)
+  struct StepIt {
+    int hg, qb;
   };
-  auto issue = [&](int s) {
-    int hq, q0;
-    step_coords(s, hq, q0);
+  auto advance = [&](StepIt& it) {
+    if (++it.qb == nM) {
+      it.qb = m_begin;
+      ++it.hg;
+    }
+  };
+
+  auto issue = [&](int s, const StepIt& it) {
+    const int hq = hkv * p.group + it.hg, q0 = it.qb * BMQ;
     char* st = smem + (s & 3) * STAGE;
     const long long off = (q_tok0 + q0) * qs + hq * D;
     const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
@@ -471,7 +460,7 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
     copy_rows_to_lds<L>(qb, bytes, st + 1 * QT + wave * L * 1024, cp.v);
     copy_rows_to_lds<L>(gb, bytes, st + 2 * QT + wave * L * 1024, cp.k);
     copy_rows_to_lds<L>(gb, bytes, st + 3 * QT + wave * L * 1024, cp.v);
-    if (!VARLEN && wave == 0) {
+    if (wave == 0) {
       const float2* sb = p.stats + ((long long)b * p.Hq + hq) * p.Sq_pad + q0;
       copy_row_to_lds(sb, (uint32_t)(p.Sq_pad - q0) * 8u, st + 4 * QT, lane < 16 ? (uint32_t)lane * 16u : 0x40000000u);
     }
@@ -479,7 +468,7 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
 
   // statistics of a step: st[2 g + j] = (lse2, delta) of query rows
   // qr + 2 j and qr + 2 j + 1, qr = 16 (g >> 1) + 8 h + 4 (g & 1)
-  auto stats_lds = [&](uint32_t sb, float4 (&st)[8]) {
+  auto stats_lds = [&](uint32_t sb, f32x4 (&st)[8]) {
     const uint32_t a = sb + 4 * QT + 64 * h;
     i32x4 r[8];
     r[0] = lds_rd128<0>(a);
@@ -491,23 +480,7 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
     r[6] = lds_rd128<160>(a);
     r[7] = lds_rd128<176>(a);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st[j] = __builtin_bit_cast(float4, r[j]);
-  };
-  // varlen: from global memory ([Hq, T]); rows past the sequence read its
-  // last row (their Q and dO are zero, so they contribute nothing)
-  auto stats_glb = [&](int s, float4 (&st)[8]) {
-    int hq, q0;
-    step_coords(s, hq, q0);
-    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = q0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + 2 * j;
-        const float2 x = sg[min(r, q_len - 1)];
-        const float2 y = sg[min(r + 1, q_len - 1)];
-        st[2 * g + j] = make_float4(x.x, x.y, y.x, y.y);
-      }
+    for (int j = 0; j < 8; ++j) st[j] = __builtin_bit_cast(f32x4, r[j]);
   };
 
   const float c = p.scale_log2;
@@ -518,12 +491,12 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
 
   // P and dS of elements E, E + 1 (E even; register r = 4 g + i holds query
   // row 16 (g >> 1) + 8 h + 4 (g & 1) + i) into the 16-bit B operands
-  auto pair = [&](auto ec, const f32x16& sc, const f32x16& pc, const float4 (&st)[8], int t, vec8 (&pvc)[2],
-                  vec8 (&dsc)[2]) {
+  auto pair = [&](auto ec, const f32x16& sc, const f32x16& pc, const f32x4 (&st)[8], int t,
+                  vec8 (&pvc)[2], vec8 (&dsc)[2]) {
     constexpr int E = decltype(ec)::value;
     constexpr int g = E >> 2, i = E & 3;
     constexpr int cr = 16 * (g >> 1) + 4 * (g & 1) + i;
-    const float4 sv = st[2 * g + (i >> 1)];
+    const f32x4 sv = st[2 * g + (i >> 1)];
     float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E], c, -sv.x));
     float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E + 1], c, -sv.z));
     p0 = t > cr ? 0.f : p0;
@@ -570,35 +543,42 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
     });
   };
 
-  // dV^T += dO^T P, dK^T += Q^T dS of the step in stage sb; with HEAD_NEXT the
-  // first row reads of the next step (stage sbn) are issued during the last
-  // channel block; HOOK(m) runs after MFMA m (4 per channel block)
-  auto dvdk = [&](auto nextc, uint32_t sb, uint32_t sbn, const vec8 (&pvp)[2], const vec8 (&dsp)[2],
-                  i32x4 (&qg)[KT][2], auto&& hook) {
-    constexpr bool NEXT = decltype(nextc)::value;
-    const uint32_t a = sb + QT + rd.voff0;
+  // transposed reads of channel block db of the step in stage sb: pairs 0, 1
+  // = dO^T, pairs 2, 3 = Q^T (16 query rows each)
+  auto tr_issue = [&](auto dbc, uint32_t sb, i16x4(&r)[8]) {
+    constexpr int db = decltype(dbc)::value;
+    constexpr int R = ROW;
+    const uint32_t x = sb + QT + (rd.voff0 ^ (uint32_t)(db << 6));
+    r[0] = lds_tr16<2 * QT>(x);
+    r[1] = lds_tr16<2 * QT + 4 * R>(x);
+    r[2] = lds_tr16<2 * QT + 16 * R>(x);
+    r[3] = lds_tr16<2 * QT + 20 * R>(x);
+    r[4] = lds_tr16<0>(x);
+    r[5] = lds_tr16<4 * R>(x);
+    r[6] = lds_tr16<16 * R>(x);
+    r[7] = lds_tr16<20 * R>(x);
+  };
+
+  // dV^T += dO^T P, dK^T += Q^T dS of the step in stage sb.  PRE: the reads
+  // of block 0 were issued by the caller (tr0).  NEXT: the first row reads of
+  // the next step (stage sbn) are issued during the last channel block.
+  // HOOK(m) runs after MFMA m (4 per channel block).
+  auto dvdk = [&](auto prec, auto nextc, uint32_t sb, uint32_t sbn, const vec8 (&pvp)[2], const vec8 (&dsp)[2],
+                  i32x4 (&qg)[KT][2], const i16x4 (&tr0)[8], auto&& hook) {
+    constexpr bool PRE = decltype(prec)::value, NEXT = decltype(nextc)::value;
     i16x4 tr[2][8];
-    auto tr_issue = [&](auto dbc, i16x4(&r)[8]) {
-      constexpr int db = decltype(dbc)::value;
-      constexpr int R = ROW;
-      const uint32_t x = sb + QT + (rd.voff0 ^ (uint32_t)(db << 6));
-      r[0] = lds_tr16<2 * QT>(x);
-      r[1] = lds_tr16<2 * QT + 4 * R>(x);
-      r[2] = lds_tr16<2 * QT + 16 * R>(x);
-      r[3] = lds_tr16<2 * QT + 20 * R>(x);
-      r[4] = lds_tr16<0>(x);
-      r[5] = lds_tr16<4 * R>(x);
-      r[6] = lds_tr16<16 * R>(x);
-      r[7] = lds_tr16<20 * R>(x);
-    };
-    (void)a;
-    tr_issue(std::integral_constant<int, 0>{}, tr[0]);
+    if constexpr (PRE) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tr[0][j] = tr0[j];
+    } else {
+      tr_issue(std::integral_constant<int, 0>{}, sb, tr[0]);
+    }
     static_for<DB>([&](auto dbc) {
       constexpr int db = decltype(dbc)::value;
       i16x4(&cur)[8] = tr[db & 1];
       constexpr int DVB = M::DV + 16 * db, DKB = M::DK + 16 * db;
       constexpr int nb = (db + 1 < DB) ? 8 : (NEXT ? 2 * HEAD : 0);
-      if constexpr (db + 1 < DB) tr_issue(std::integral_constant<int, db + 1>{}, tr[(db + 1) & 1]);
+      if constexpr (db + 1 < DB) tr_issue(std::integral_constant<int, db + 1>{}, sb, tr[(db + 1) & 1]);
       else if constexpr (NEXT) rowread_head(sbn, qg);
       lds_wait<6 + nb>(cur);
       mfma_acc<T, DVB>(tr_pair<vec8>(cur, 0), pvp[0]);
@@ -619,32 +599,49 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   };
   auto no_hook = [](auto) {};
 
-  // one iteration: P, dS of step s (from sc, pc, stc) into pvc, dsc, under
-  // dV/dK of step s - 1 (pvp, dsp) and S, dP of step s + 1 (into sn, pn)
+  // one iteration: P, dS of step s (from sc, pc, st) into pvc, dsc, under
+  // dV/dK of step s - 1 (pvp, dsp; its first reads in trn) and S, dP of step
+  // s + 1 (into sn, pn).  With NEXT, ends by issuing the statistics of step
+  // s + 1 (into st, after their last use for step s) and the first
+  // transposed reads of dV/dK(s) (into trn).  it: step s; it2: step s + 2
+  // (copy); each advanced by one.
   auto body = [&](auto prevc, auto nextc, int s, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
                   const vec8 (&pvp)[2], const vec8 (&dsp)[2], vec8 (&pvc)[2], vec8 (&dsc)[2],
-                  const float4 (&stc)[8], float4 (&stn)[8]) {
+                  f32x4 (&st)[8], i16x4 (&trn)[8], StepIt& it, StepIt& it2) {
     constexpr bool PREV = decltype(prevc)::value, NEXT = decltype(nextc)::value;
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (VARLEN && NEXT) stats_glb(s + 1, stn);
-    if (s + 2 < nsteps) issue(s + 2);
     const uint32_t sbn = stage(s + 1);
-    if constexpr (!VARLEN && NEXT) stats_lds(sbn, stn);
-    int hq, q0;
-    step_coords(s, hq, q0);
-    const int t = tl - q0;
+    const int t = tl - it.qb * BMQ;
     i32x4 qg[KT][2];
-    __builtin_amdgcn_sched_barrier(0);
-    // rows 0-15: pairs 0..3
-    auto hook1 = [&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      if constexpr ((m + 1) % DB == 0) pair(std::integral_constant<int, 2 * ((m + 1) / DB - 1)>{}, sc, pc, stc, t, pvc, dsc);
+    auto copy_next = [&]() {
+      if (s + 2 < nsteps) issue(s + 2, it2);
     };
+    // The vector work reads S and dP through this tie, placed after the wait
+    // that covers the statistics reads: its inputs are otherwise available
+    // (to the compiler) at the end of the previous iteration, and it may
+    // hoist the pure arithmetic there, ahead of the waits and of the MFMA
+    // results.  (Tying the statistics as well gave wrong dV in measurement;
+    // the tie on S and dP alone already orders every use.)
+    f32x16 scx = sc, pcx = pc;
+    auto tie = [&]() { asm volatile("" : "+v"(scx), "+v"(pcx)); };
+    // rows 0-15: pairs 0..3
     if constexpr (PREV) {
-      dvdk(nextc, stage(s - 1), sbn, pvp, dsp, qg, hook1);
+      dvdk(std::true_type{}, nextc, stage(s - 1), sbn, pvp, dsp, qg, trn, [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m == 0) {
+          tie();
+          copy_next();
+        }
+        if constexpr ((m + 1) % DB == 0)
+          pair(std::integral_constant<int, 2 * ((m + 1) / DB - 1)>{}, scx, pcx, st, t, pvc, dsc);
+      });
     } else {
+      tie();
+      copy_next();
       if constexpr (NEXT) rowread_head(sbn, qg);
-      static_for<4>([&](auto e) { pair(std::integral_constant<int, 2 * decltype(e)::value>{}, sc, pc, stc, t, pvc, dsc); });
+      static_for<4>([&](auto e) {
+        pair(std::integral_constant<int, 2 * decltype(e)::value>{}, scx, pcx, st, t, pvc, dsc);
+      });
       __builtin_amdgcn_sched_barrier(0);
     }
     // rows 16-31: pairs 4..7
@@ -652,48 +649,56 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
       sdp(sbn, sn, pn, qg, [&](auto kkc) {
         constexpr int kk = decltype(kkc)::value;
         constexpr int per = KT / 4;
-        if constexpr ((kk + 1) % per == 0) pair(std::integral_constant<int, 8 + 2 * ((kk + 1) / per - 1)>{}, sc, pc, stc, t, pvc, dsc);
+        if constexpr ((kk + 1) % per == 0)
+          pair(std::integral_constant<int, 8 + 2 * ((kk + 1) / per - 1)>{}, scx, pcx, st, t, pvc, dsc);
       });
-      pad2(sn, pn);
+      stats_lds(sbn, st);
+      tr_issue(std::integral_constant<int, 0>{}, stage(s), trn);
     } else {
-      static_for<4>([&](auto e) { pair(std::integral_constant<int, 8 + 2 * decltype(e)::value>{}, sc, pc, stc, t, pvc, dsc); });
+      static_for<4>([&](auto e) {
+        pair(std::integral_constant<int, 8 + 2 * decltype(e)::value>{}, scx, pcx, st, t, pvc, dsc);
+      });
     }
+    advance(it);
+    advance(it2);
   };
 
   const std::integral_constant<bool, true> yes;
   const std::integral_constant<bool, false> no;
   f32x16 sa, pa, sb2, pb2;
   vec8 px[2], dx[2], py[2], dy[2];
-  float4 sta[8], stb[8];
+  f32x4 st[8];
+  i16x4 trn[8];
   i32x4 qg0[KT][2];
   if (nsteps > 0) {
-    issue(0);
-    if (nsteps > 1) issue(1);
-    if constexpr (VARLEN) stats_glb(0, sta);
+    StepIt it{0, m_begin}, it2{0, m_begin};
+    issue(0, it2);
+    advance(it2);
+    if (nsteps > 1) issue(1, it2);
+    advance(it2);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (!VARLEN) stats_lds(stage(0), sta);
+    stats_lds(stage(0), st);
     rowread_head(stage(0), qg0);
     sdp(stage(0), sa, pa, qg0, no_hook);
     pad2(sa, pa);
-    // step s consumes S set s % 2 (a, b), produces P set s % 2 (x, y) and
-    // statistics set (s + 1) % 2
+    // step s consumes S set s % 2 (a, b) and produces P set s % 2 (x, y)
     if (nsteps == 1) {
-      body(no, no, 0, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
-      dvdk(no, stage(0), 0, px, dx, qg0, no_hook);
+      body(no, no, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+      dvdk(no, no, stage(0), 0, px, dx, qg0, trn, no_hook);
     } else {
-      body(no, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+      body(no, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
       int s = 1;
       for (; s + 2 < nsteps; s += 2) {
-        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
-        body(yes, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
+        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
       }
       if (s + 1 < nsteps) {
-        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
-        body(yes, no, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, sta, stb);
-        dvdk(no, stage(s + 1), 0, px, dx, qg0, no_hook);
+        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, no, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+        dvdk(no, no, stage(s + 1), 0, px, dx, qg0, trn, no_hook);
       } else {
-        body(yes, no, s, sb2, pb2, sa, pa, px, dx, py, dy, stb, sta);
-        dvdk(no, stage(s), 0, py, dy, qg0, no_hook);
+        body(yes, no, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        dvdk(no, no, stage(s), 0, py, dy, qg0, trn, no_hook);
       }
     }
   }
@@ -725,12 +730,12 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
-  if constexpr (D == 128) {
+  if constexpr (D == 128 && !VARLEN) {
     constexpr int lds = 4 * (4 * 32 * 2 * D + 1024);
-    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_pipe_kernel<T, D, CAUSAL, VARLEN>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_pipe_kernel<T, D, CAUSAL>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<T, D, CAUSAL, VARLEN>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<T, D, CAUSAL>), dim3(p.grid_dkdv), dim3(256), lds, s, p);
   } else {
     constexpr int lds = 2 * (4 * 32 * 2 * D + 1024);
     static const hipError_t attr = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>,
