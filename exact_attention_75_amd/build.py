@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip",
-           "attn_bwd_dkdv.hip"]
+           "attn_bwd_dkdv.hip", "attn_bwd_dq.hip"]
 ARCH = "gfx950"
 
 
@@ -65,7 +65,7 @@ def compile_one(src: str, save_temps: str | None) -> str:
 
 # Sources whose kernels keep data in AGPRs named in inline assembly: the
 # compiler must not use any AGPR itself there (see csrc/wide_regs.h).
-PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip", "attn_bwd_dkdv.hip"]
+PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip", "attn_bwd_dkdv.hip", "attn_bwd_dq.hip"]
 
 
 def check_pinned_agprs(src: str) -> None:
@@ -113,7 +113,7 @@ def build(jobs: int = 4, save_temps: str | None = None) -> str:
 
 
 EXPECTED_KERNELS = ("fwd_kernel", "fwd_wide_kernel", "fwd_fp8_kernel", "prepass_kernel", "combine_kernel",
-                    "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
+                    "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dkdv_pipe_kernel", "bwd_dq_pipe_kernel")
 
 
 def check_kernels(path: str) -> None:

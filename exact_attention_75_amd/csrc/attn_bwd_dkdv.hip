@@ -42,106 +42,29 @@
 #include "bwd_common.h"
 #include "kernel_common.h"
 #include "kernels.h"
+#include "bwd_regs.h"
 #include "wide_regs.h"
 
 namespace attn {
 namespace dkdv {
 
-using wide::Asm;
+using namespace breg;
 
+// AGPR map (DB = D / 32 channel blocks, KT = D / 16 k-steps)
 template <int D>
 struct Map {
   static constexpr int DB = D / 32, KT = D / 16;
   static constexpr int DV = 0, DK = 16 * DB, KF = 32 * DB, VF = 32 * DB + 4 * KT;
+  static constexpr int USED = VF + 4 * KT;
 };
+static_assert(Map<64>::USED == 96, "d = 64 register map");
+static_assert(Map<128>::USED <= 256, "d = 128 register map");
 
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-  }(std::make_integer_sequence<int, N>{});
-}
-
-// fragment (K or V) k-step kk -> its four AGPRs
-template <int BASE, int KK>
-constexpr Asm frag_load_text() {
-  Asm t;
-  t.s("global_load_dwordx4 ").a(BASE + 4 * KK, 4).s(", %0, off");
-  return t;
-}
-template <int BASE, int KK>
-__device__ __forceinline__ void frag_load(const void* ptr) {
-  asm volatile((frag_load_text<BASE, KK>())::"v"(ptr) : "memory");
-}
-
-// accumulators a[0 : 32 DB) = 0.  The clobber list reserves the AGPRs the
-// map uses (the compiler does not read the assembly text): all 256 for
-// d = 128, a0..a95 for d = 64, which leaves room for two waves per SIMD.
-#define DKDV_CLOBBER_AGPRS_96                                                                            \
-  "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", ATTN_AGPRS_10(1), ATTN_AGPRS_10(2),         \
-      ATTN_AGPRS_10(3), ATTN_AGPRS_10(4), ATTN_AGPRS_10(5), ATTN_AGPRS_10(6), ATTN_AGPRS_10(7), ATTN_AGPRS_10(8), \
-      "a90", "a91", "a92", "a93", "a94", "a95"
-static_assert(Map<64>::VF + 4 * Map<64>::KT == 96, "d = 64 register map");
-static_assert(Map<128>::VF + 4 * Map<128>::KT <= 256, "d = 128 register map");
-
-template <int D>
-constexpr Asm zero_text() {
-  Asm t;
-  for (int r = 0; r < 32 * Map<D>::DB; ++r) t.s("v_accvgpr_write_b32 a").i(r).s(", 0\n\t");
-  return t;
-}
+// accumulators a[0 : 32 DB) = 0, reserving the AGPRs the map uses: all 256
+// for d = 128, a0..a95 for d = 64 (room for two waves per SIMD)
 template <int D>
 __device__ __forceinline__ void acc_zero() {
-  if constexpr (D == 64) asm volatile((zero_text<D>())::: DKDV_CLOBBER_AGPRS_96);
-  else asm volatile((zero_text<D>())::: ATTN_CLOBBER_AGPRS);
-}
-
-// S or dP (VGPRs) = / += row operand (VGPR) x fragment k-step kk (AGPR)
-template <typename T, int BASE, int KK, bool FIRST>
-constexpr Asm first_text() {
-  Asm t;
-  t.s(wide::mfma_name<T>()).s("%0, %1, ").a(BASE + 4 * KK, 4).s(FIRST ? ", 0" : ", %0");
-  return t;
-}
-template <typename T, int BASE, int KK, bool FIRST, typename V8>
-__device__ __forceinline__ void mfma_first(f32x16& acc, const V8& a) {
-  if constexpr (FIRST) asm volatile((first_text<T, BASE, KK, true>()) : "=&v"(acc) : "v"(a));
-  else asm volatile((first_text<T, BASE, KK, false>()) : "+v"(acc) : "v"(a));
-}
-
-// accumulator block at AGPR ACC += A (VGPR) x B (VGPR)
-template <typename T, int ACC>
-constexpr Asm acc_text() {
-  Asm t;
-  t.s(wide::mfma_name<T>()).a(ACC, 16).s(", %0, %1, ").a(ACC, 16);
-  return t;
-}
-template <typename T, int ACC, typename V8>
-__device__ __forceinline__ void mfma_acc(const V8& a, const V8& b) {
-  asm volatile((acc_text<T, ACC>())::"v"(a), "v"(b));
-}
-
-// s_nop run after MFMAs before their results are read by vector code
-__device__ __forceinline__ void pad2(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
-}
-
-template <int ACC>
-constexpr Asm read_text() {
-  Asm t;
-  for (int e = 0; e < 16; ++e) {
-    t.s("v_accvgpr_read_b32 %").i(e).s(", a").i(ACC + e);
-    if (e < 15) t.s("\n\t");
-  }
-  return t;
-}
-template <int ACC>
-__device__ __forceinline__ f32x16 acc_read() {
-  float x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15;
-  asm volatile((read_text<ACC>())
-               : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7), "=v"(x8),
-                 "=v"(x9), "=v"(x10), "=v"(x11), "=v"(x12), "=v"(x13), "=v"(x14), "=v"(x15));
-  return f32x16{x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15};
+  breg::acc_zero<32 * Map<D>::DB, D == 64 ? 96 : 256>();
 }
 
 }  // namespace dkdv

@@ -1,5 +1,5 @@
 // bwd_common.h -- LDS tile helpers shared by the backward kernels
-// (attn_bwd.hip, attn_bwd_dkdv.hip).
+// (attn_bwd_dkdv.hip, attn_bwd_dq.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>

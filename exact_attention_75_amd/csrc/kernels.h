@@ -124,6 +124,8 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int causal, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
 // dK, dV of the backward alone (the statistics must already be written)
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
+// dQ of the backward alone (the statistics must already be written)
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s);
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
 constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);
