@@ -359,15 +359,28 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
   auto stage = [&](int s) { return lds0 + (uint32_t)(s & 3) * STAGE; };
 
-  // step s = (query head hkv * group + hg, query block qb), advanced by one
-  // step at a time (steps walk the blocks of one head, then the next head)
+  // Step order: first the query blocks a mask reaches (nd per head: the
+  // causal diagonal, every block of a ragged key block) of every head, then
+  // the other blocks of every head; steps [0, nmask) need the mask.
+  // StepIt = (query head hkv * group + hg, query block qb) of one step,
+  // advanced one step at a time over blocks [lo, hi) of each head.
+  const bool ragged = k0 + kBwdBlockN > k_len;
+  const int nd = ragged ? per_head : (CAUSAL ? min(per_head, 4) : 0);
+  const bool two_phase = nd > 0 && nd < per_head;
+  const int nmask = nd == 0 ? 0 : (two_phase ? p.group * nd : nsteps);
   struct StepIt {
-    int hg, qb;
+    int hg, qb, lo, hi;
   };
   auto advance = [&](StepIt& it) {
-    if (++it.qb == nM) {
-      it.qb = m_begin;
-      ++it.hg;
+    if (++it.qb < it.hi) return;
+    if (++it.hg < p.group) {
+      it.qb = it.lo;
+      return;
+    }
+    if (it.hi != nM) {                    // end of the first phase
+      it.hg = 0;
+      it.lo = it.qb = it.hi;
+      it.hi = nM;
     }
   };
 
@@ -414,16 +427,19 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
 
   // P and dS of elements E, E + 1 (E even; register r = 4 g + i holds query
   // row 16 (g >> 1) + 8 h + 4 (g & 1) + i) into the 16-bit B operands
-  auto pair = [&](auto ec, const f32x16& sc, const f32x16& pc, const f32x4 (&st)[8], int t,
+  auto pair = [&](auto ec, auto maskc, const f32x16& sc, const f32x16& pc, const f32x4 (&st)[8], int t,
                   vec8 (&pvc)[2], vec8 (&dsc)[2]) {
     constexpr int E = decltype(ec)::value;
+    constexpr bool MASK = decltype(maskc)::value;
     constexpr int g = E >> 2, i = E & 3;
     constexpr int cr = 16 * (g >> 1) + 4 * (g & 1) + i;
     const f32x4 sv = st[2 * g + (i >> 1)];
     float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E], c, -sv.x));
     float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[E + 1], c, -sv.z));
-    p0 = t > cr ? 0.f : p0;
-    p1 = t > cr + 1 ? 0.f : p1;
+    if constexpr (MASK) {
+      p0 = t > cr ? 0.f : p0;
+      p1 = t > cr + 1 ? 0.f : p1;
+    }
     const float d0 = p0 * (pc[E] - sv.y);
     const float d1 = p1 * (pc[E + 1] - sv.w);
     constexpr int v = g >> 1, o = 4 * (g & 1) + i;
@@ -528,7 +544,7 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   // s + 1 (into st, after their last use for step s) and the first
   // transposed reads of dV/dK(s) (into trn).  it: step s; it2: step s + 2
   // (copy); each advanced by one.
-  auto body = [&](auto prevc, auto nextc, int s, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
+  auto body = [&](auto prevc, auto nextc, auto maskc, int s, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn,
                   const vec8 (&pvp)[2], const vec8 (&dsp)[2], vec8 (&pvc)[2], vec8 (&dsc)[2],
                   f32x4 (&st)[8], i16x4 (&trn)[8], StepIt& it, StepIt& it2) {
     constexpr bool PREV = decltype(prevc)::value, NEXT = decltype(nextc)::value;
@@ -545,7 +561,8 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
     // hoist the pure arithmetic there, ahead of the waits and of the MFMA
     // results.  (Tying the statistics as well gave wrong dV in measurement;
     // the tie on S and dP alone already orders every use.)
-    f32x16 scx = sc, pcx = pc;
+    f32x16& scx = sc;
+    f32x16& pcx = pc;
     auto tie = [&]() { asm volatile("" : "+v"(scx), "+v"(pcx)); };
     // rows 0-15: pairs 0..3
     if constexpr (PREV) {
@@ -556,14 +573,14 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
           copy_next();
         }
         if constexpr ((m + 1) % DB == 0)
-          pair(std::integral_constant<int, 2 * ((m + 1) / DB - 1)>{}, scx, pcx, st, t, pvc, dsc);
+          pair(std::integral_constant<int, 2 * ((m + 1) / DB - 1)>{}, maskc, scx, pcx, st, t, pvc, dsc);
       });
     } else {
       tie();
       copy_next();
       if constexpr (NEXT) rowread_head(sbn, qg);
       static_for<4>([&](auto e) {
-        pair(std::integral_constant<int, 2 * decltype(e)::value>{}, scx, pcx, st, t, pvc, dsc);
+        pair(std::integral_constant<int, 2 * decltype(e)::value>{}, maskc, scx, pcx, st, t, pvc, dsc);
       });
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -573,13 +590,13 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
         constexpr int kk = decltype(kkc)::value;
         constexpr int per = KT / 4;
         if constexpr ((kk + 1) % per == 0)
-          pair(std::integral_constant<int, 8 + 2 * ((kk + 1) / per - 1)>{}, scx, pcx, st, t, pvc, dsc);
+          pair(std::integral_constant<int, 8 + 2 * ((kk + 1) / per - 1)>{}, maskc, scx, pcx, st, t, pvc, dsc);
       });
       stats_lds(sbn, st);
       tr_issue(std::integral_constant<int, 0>{}, stage(s), trn);
     } else {
       static_for<4>([&](auto e) {
-        pair(std::integral_constant<int, 8 + 2 * decltype(e)::value>{}, scx, pcx, st, t, pvc, dsc);
+        pair(std::integral_constant<int, 8 + 2 * decltype(e)::value>{}, maskc, scx, pcx, st, t, pvc, dsc);
       });
     }
     advance(it);
@@ -594,7 +611,8 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
   i16x4 trn[8];
   i32x4 qg0[KT][2];
   if (nsteps > 0) {
-    StepIt it{0, m_begin}, it2{0, m_begin};
+    const StepIt it0{0, m_begin, m_begin, two_phase ? m_begin + nd : nM};
+    StepIt it = it0, it2 = it0;
     issue(0, it2);
     advance(it2);
     if (nsteps > 1) issue(1, it2);
@@ -604,23 +622,29 @@ bwd_dkdv_pipe_kernel(BwdParams p) {
     rowread_head(stage(0), qg0);
     sdp(stage(0), sa, pa, qg0, no_hook);
     pad2(sa, pa);
-    // step s consumes S set s % 2 (a, b) and produces P set s % 2 (x, y)
+    // step s consumes S set s % 2 (a, b) and produces P set s % 2 (x, y);
+    // the first and the last steps, and pairs that start below nmask, run
+    // with the mask
     if (nsteps == 1) {
-      body(no, no, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+      body(no, no, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
       dvdk(no, no, stage(0), 0, px, dx, qg0, trn, no_hook);
     } else {
-      body(no, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+      body(no, yes, yes, 0, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
       int s = 1;
+      for (; s + 2 < nsteps && s < nmask; s += 2) {
+        body(yes, yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, yes, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+      }
       for (; s + 2 < nsteps; s += 2) {
-        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
-        body(yes, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+        body(yes, yes, no, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, yes, no, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
       }
       if (s + 1 < nsteps) {
-        body(yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
-        body(yes, no, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
+        body(yes, yes, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, no, yes, s + 1, sa, pa, sb2, pb2, py, dy, px, dx, st, trn, it, it2);
         dvdk(no, no, stage(s + 1), 0, px, dx, qg0, trn, no_hook);
       } else {
-        body(yes, no, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
+        body(yes, no, yes, s, sb2, pb2, sa, pa, px, dx, py, dy, st, trn, it, it2);
         dvdk(no, no, stage(s), 0, py, dy, qg0, trn, no_hook);
       }
     }
