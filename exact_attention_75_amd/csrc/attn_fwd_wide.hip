@@ -24,8 +24,12 @@
 //    direct-to-LDS copies.  Every round issues the same copies (a copy past
 //    the last tile has an empty buffer range and writes zeros into a free
 //    buffer), so the loop has no branches around them.
-//  * The running max moves lazily (only when a row's max grows by more than
-//    2^8 in probability), so P <= 256 and the O rescale is a rare branch.
+//  * The running max is exact after the first key tile and then moves only
+//    when a tile's probabilities, taken against the current max, sum to more
+//    than PMAX in some lane: the sum bounds every probability of the tile, so
+//    no per-tile row max is needed (P <= PMAX, far inside the fp32, bf16 and
+//    fp16 ranges).  Then -- rarely -- the tile's row max is taken, O and l
+//    are rescaled and the tile's probabilities recomputed.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -64,7 +68,7 @@ fwd_wide_kernel(FwdParams p) {
 #define ATTN_WIDE_STAGES 4
 #endif
   constexpr int STAGES = ATTN_WIDE_STAGES;   // K and V ring depth
-  constexpr float TAU = 8.0f;
+  constexpr float PMAX = 16384.0f;       // bound on a lane's share of a tile's probability sum
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(LOADS == 4 && QB == 2 && DB == 4 && NB == 2 && KT == 8, "tile shape");
   // [K ring | V ring]
@@ -196,15 +200,14 @@ fwd_wide_kernel(FwdParams p) {
   // ---------------------------------------------------------------- softmax state
   const float c = p.scale_log2;
   // per query block: running max (scale*log2e units), this lane half's share
-  // of the running sum over the fp32 probabilities, the exponent offset of
-  // the current tile and the factor O still owes for the last max move
-  float m_run[QB], l_run[QB], msub[QB], alpha[QB];
+  // of the running sum over the fp32 probabilities, and the exponent offset
+  // of the current tile
+  float m_run[QB], l_run[QB], msub[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = NEG_INF;
     l_run[qb] = 0.f;
     msub[qb] = 0.f;
-    alpha[qb] = 1.f;
   }
 
   // mask: element i of s[qb][bb] is key j0 + 32 bb + 16 (i/8) + 8 h + i%8 for
@@ -230,9 +233,8 @@ fwd_wide_kernel(FwdParams p) {
       }
     }
   };
-  // row max of block qb in four parts of 8 elements, then across the lane
-  // halves and the lazy, wave-uniform decision to move the running max; l
-  // first picks up the pending sums of the previous tile (rs_prev)
+  // first tile: row max of block qb in four parts of 8 elements, then across
+  // the lane halves, and the running max set from it
   float mxp[QB];
   auto max_part = [&](f32x16(&sn)[QB][NB], int qb, int part) {
     if (part == 0) mxp[qb] = NEG_INF;
@@ -240,16 +242,10 @@ fwd_wide_kernel(FwdParams p) {
     for (int k = 0; k < 8; ++k) mxp[qb] = fmaxf(mxp[qb], sn[qb][part >> 1][8 * (part & 1) + k]);
     keep(mxp[qb]);
   };
-  auto finish_max = [&](int qb, float rs_prev) {
+  auto finish_max = [&](int qb) {
     const float mx = fmaxf(mxp[qb], wave_half_swap(mxp[qb]));
-    const float m_new = fmaxf(m_run[qb], mx * c);
-    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run[qb] + TAU) != 0;
-    const float m_upd = moved ? m_new : m_run[qb];
-    const float a = (m_upd == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_upd);
-    alpha[qb] = a;
-    l_run[qb] = (l_run[qb] + rs_prev) * a;
-    m_run[qb] = m_upd;
-    msub[qb] = (m_upd == NEG_INF) ? 0.f : m_upd;
+    m_run[qb] = mx * c;
+    msub[qb] = (m_run[qb] == NEG_INF) ? 0.f : m_run[qb];
     keep(msub[qb]);
   };
   // exp2(c s - m) of element e of chunk (qb, cc), added to the row sum and
@@ -297,7 +293,55 @@ fwd_wide_kernel(FwdParams p) {
   // One iteration.  HS: S_t is computed (t < n_w); HP: tile
   // t-1 is finished and P_{t-1} V_{t-1} added (t >= 1).  s_cur / p_cur
   // receive tile t, s_prev / p_prev hold tile t-1.
-  float rs_a[QB] = {0.f, 0.f};   // sums of P_{t-1} computed in A (added before l's rescale)
+  float rs_a[QB] = {0.f, 0.f};     // sums of P_{t-1} computed in A
+  float rs_pend[QB] = {0.f, 0.f};  // sums of chunk 0 of the tile computed in the previous B
+  // Tile t-1 is complete (all its probabilities taken against msub): l takes
+  // its sum, unless some lane's share exceeds PMAX (or is not finite).  Then
+  // the running max moves to the tile's row max, O and l are rescaled, and
+  // the tile's probabilities and sum are recomputed.
+  auto check = [&](f32x16(&sp)[QB][NB], vec8(&pp)[QB][NC]) {
+    float part[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) part[qb] = rs_pend[qb] + rs_a[qb];
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(part[0] <= PMAX) || !(part[1] <= PMAX)) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      float a[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sp[qb][bb][i]);
+        mx = fmaxf(mx, wave_half_swap(mx));
+        const float m_new = fmaxf(m_run[qb], mx * c);
+        a[qb] = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= a[qb];
+        m_run[qb] = m_new;
+        msub[qb] = (m_new == NEG_INF) ? 0.f : m_new;
+        float sum = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[qb][cc >> 1][8 * (cc & 1) + e], c, -msub[qb]));
+            pp[qb][cc][e] = (T)x;
+            sum += x;
+          }
+        part[qb] = sum;
+      }
+      acc_scale<0, 0>(a[0]);
+      acc_scale<0, 1>(a[0]);
+      acc_scale<0, 2>(a[0]);
+      acc_scale<0, 3>(a[0]);
+      acc_scale<1, 0>(a[1]);
+      acc_scale<1, 1>(a[1]);
+      acc_scale<1, 2>(a[1]);
+      acc_scale<1, 3>(a[1]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
+  };
   auto iter = [&](int t, auto hs_tag, auto hp_tag, f32x16(&s_cur)[QB][NB],
                   f32x16(&s_prev)[QB][NB], vec8(&p_cur)[QB][NC], vec8(&p_prev)[QB][NC]) {
     constexpr bool HS = decltype(hs_tag)::value;
@@ -313,20 +357,6 @@ fwd_wide_kernel(FwdParams p) {
     }
     const uint32_t kst = (uint32_t)(slot_of(t) * TILE);       // K_t
     const uint32_t vst = (uint32_t)(slot_of(t - 1) * TILE);   // V_{t-1}
-    // O owes the rescale decided with the max of tile t-1 (rare)
-    if constexpr (HP) {
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0, 0)) {
-        acc_scale<0, 0>(alpha[0]);
-        acc_scale<0, 1>(alpha[0]);
-        acc_scale<0, 2>(alpha[0]);
-        acc_scale<0, 3>(alpha[0]);
-        acc_scale<1, 0>(alpha[1]);
-        acc_scale<1, 1>(alpha[1]);
-        acc_scale<1, 2>(alpha[1]);
-        acc_scale<1, 3>(alpha[1]);
-      }
-      alpha[0] = alpha[1] = 1.f;
-    }
     rs_a[0] = rs_a[1] = 0.f;
     float rs_b[QB] = {0.f, 0.f};
 
@@ -387,19 +417,21 @@ fwd_wide_kernel(FwdParams p) {
       commit(pa, rs_a, p_prev);
     }
 
-    // ---- B: P_{t-1} V_{t-1}; mask, row max and exp2 of chunk 0 of S_t
+    if constexpr (HP) check(s_prev, p_prev);
+
+    // ---- B: P_{t-1} V_{t-1}; mask and exp2 of chunk 0 of S_t
     // vector work of slot j of chunk CC (after the chunk's j-th MFMA)
     auto slot = [&](auto cc_tag, auto j_tag) {
       constexpr int CC = decltype(cc_tag)::value;
       constexpr int J = decltype(j_tag)::value;
       if constexpr (HS) {
-        if constexpr (CC == 1) {
+        if constexpr (CC == 1 && !HP) {
           if constexpr (J == 0) { max_part(s_cur, 0, 0); max_part(s_cur, 0, 1); }
           if constexpr (J == 1) { max_part(s_cur, 0, 2); max_part(s_cur, 0, 3); }
-          if constexpr (J == 2) finish_max(0, rs_a[0]);
+          if constexpr (J == 2) finish_max(0);
           if constexpr (J == 3) { max_part(s_cur, 1, 0); max_part(s_cur, 1, 1); }
           if constexpr (J == 4) { max_part(s_cur, 1, 2); max_part(s_cur, 1, 3); }
-          if constexpr (J == 5) finish_max(1, rs_a[1]);
+          if constexpr (J == 5) finish_max(1);
         }
         if constexpr (CC == 2) ex1(pb, s_cur, 0, 0, J, rs_b, p_cur);
         if constexpr (CC == 3) ex1(pb, s_cur, 1, 0, J, rs_b, p_cur);
@@ -462,8 +494,8 @@ fwd_wide_kernel(FwdParams p) {
       for (int e = 0; e < 8; ++e) ex1(pb, s_cur, 1, 0, e, rs_b, p_cur);
       commit(pb, rs_b, p_cur);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs_b[qb] + (HS ? 0.f : rs_a[qb]);
+    rs_pend[0] = rs_b[0];
+    rs_pend[1] = rs_b[1];
   };
 
   // ---------------------------------------------------------------- key loop

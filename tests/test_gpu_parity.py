@@ -113,6 +113,34 @@ def test_scale_other_than_default(ea):
     compare(o, lse, o_ref, l_ref, "scale 0.3")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_moves(ea, dtype, causal):
+    # channel 0 holds q = 1 and k = alpha * (128 * (j // 128)): every row's
+    # scores step up by `step` log2 units at each 128-key boundary, so the
+    # running max has to move again and again, by more than any lazy
+    # threshold, while a row still averages the many keys of its last step.
+    # Causal rows within 32 keys of a step boundary see only a few keys of
+    # their top step, where bf16 rounding of P alone reaches the O gate:
+    # those rows are left out of the comparison.
+    B, S, Hq, Hkv, d = 1, 1100, 4, 2, 128
+    q, k, v = W.make_dense(B, S, S, Hq, Hkv, d, dtype, seed=12)
+    scale = 1 / math.sqrt(d)
+    rows = np.arange(S)
+    if causal:
+        rows = rows[rows % 128 >= 32]
+    for step in (20.0, 60.0):
+        alpha = step / (scale * math.log2(math.e) * 128)
+        q2, k2 = q.clone(), k.clone()
+        q2[..., 0] = 1.0
+        k2[..., 0] = (alpha * 128 * (torch.arange(S, dtype=torch.float64) // 128)).view(1, S, 1).to(k.dtype)
+        print(f"[case] running max moves {dtype} causal={causal} step={step}", flush=True)
+        o, lse = run_dense(ea, q2, k2, v, causal)
+        o_ref, l_ref = A.attention(q2, k2, v, scale, causal, rows=rows)
+        compare(o[:, rows], lse[:, :, rows], o_ref[:, rows], l_ref[:, :, rows],
+                f"max moves {dtype} c{int(causal)} step {step}")
+
+
 def test_deterministic(ea):
     q, k, v = W.make_dense(2, 1000, 1000, 4, 2, 128, "bf16", seed=9)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
