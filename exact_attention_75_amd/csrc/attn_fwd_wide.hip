@@ -14,9 +14,10 @@
 //    clock as the LDS delivers.  Q stays in registers for the whole loop.
 //  * With one wave per SIMD all overlap of matrix and vector work happens
 //    inside the wave.  Iteration t runs
-//        A: S_t = K_t Q^T (32 MFMA)        with exp2 of 3/4 of S_{t-1}
-//        B: O += P_{t-1} V_{t-1} (32 MFMA) with the mask and row max of S_t
-//                                          and exp2 of its first quarter
+//        A: S_t = K_t Q^T (32 MFMA)        with exp2 of the second half of
+//                                          S_{t-1}; then the check of tile t-1
+//        B: O += P_{t-1} V_{t-1} (32 MFMA) with the mask of S_t and exp2 of
+//                                          its first half
 //    so the softmax of a tile runs under the matrix products of the two
 //    stretches around it (the pages' overlap of the GEMMs with the softmax,
 //    "flash-attention-3", "Why a schedule", within one instruction stream).
@@ -68,6 +69,14 @@ fwd_wide_kernel(FwdParams p) {
 #define ATTN_WIDE_STAGES 4
 #endif
   constexpr int STAGES = ATTN_WIDE_STAGES;   // K and V ring depth
+#ifndef ATTN_WIDE_NBX
+#define ATTN_WIDE_NBX 4
+#endif
+  // The 64 exponentials per lane of a tile come in 8 groups of 8: group g is
+  // chunk g / 2 of query block g % 2.  The first NBX groups of S_t run in
+  // stretch B of iteration t, the other groups in stretch A of iteration t+1.
+  constexpr int NBX = ATTN_WIDE_NBX;
+  constexpr int EA = 8 - NBX;          // exponentials per k-step of A
   constexpr float PMAX = 16384.0f;       // bound on a lane's share of a tile's probability sum
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(LOADS == 4 && QB == 2 && DB == 4 && NB == 2 && KT == 8, "tile shape");
@@ -360,15 +369,24 @@ fwd_wide_kernel(FwdParams p) {
     rs_a[0] = rs_a[1] = 0.f;
     float rs_b[QB] = {0.f, 0.f};
 
-    // exponentials of S_{t-1} done in A: 48 elements, chunks 1-3 of both
-    // query blocks in the order (0,1) (1,1) (0,2) (1,2) (0,3) (1,3)
+    // exponentials of S_{t-1} done in A: groups NBX .. 7
     Pend pa{0.f, 0, 0, 0, false}, pb{0.f, 0, 0, 0, false};
     auto ex_a = [&](int i) {
+      const int g = NBX + (i >> 3);
+      ex1(pa, s_prev, g & 1, g >> 1, i & 7, rs_a, p_prev);
+    };
+    // exponentials of S_t done in B: groups 0 .. NBX-1
+    auto ex_b = [&](int i) {
       const int g = i >> 3;
-      ex1(pa, s_prev, g & 1, 1 + (g >> 1), i & 7, rs_a, p_prev);
+      ex1(pb, s_cur, g & 1, g >> 1, i & 7, rs_b, p_cur);
+    };
+    // A's exponentials after MFMA j of k-step KK
+    auto ex_a_after = [&](int kk, int j) {
+#pragma unroll
+      for (int i = EA * kk + (EA * j) / 4; i < EA * kk + (EA * (j + 1)) / 4; ++i) ex_a(i);
     };
 
-    // ---- A: S_t = K_t Q^T, 6 exponentials of S_{t-1} per k-step
+    // ---- A: S_t = K_t Q^T, EA exponentials of S_{t-1} per k-step
     if constexpr (HS) {
       read_k(kst, ic<0>{});
       read_k(kst, ic<1>{});
@@ -382,23 +400,23 @@ fwd_wide_kernel(FwdParams p) {
         // LDS reads issued after k-step KK: up to two k-steps, and V chunk 0
         constexpr int LEFT = 2 * ((KK + 2 < KT ? KK + 2 : KT - 1) - KK) + ((HP && KK >= KT - 2) ? 2 * DB : 0);
         lgkm_wait<LEFT>();
-        // MFMA (bb, qb) with 2, 1, 2, 1 exponentials after it (the
-        // scheduling barriers keep each group behind its MFMA)
+        // MFMA (bb, qb), each with its share of the exponentials after it
+        // (the scheduling barriers keep each group behind its MFMA)
         mfma_s<T, F, R, 0, 0, KK>(s_cur[0][0]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (HP) { ex_a(6 * KK + 0); ex_a(6 * KK + 1); }
+        if constexpr (HP) ex_a_after(KK, 0);
         __builtin_amdgcn_sched_barrier(0);
         mfma_s<T, F, R, 0, 1, KK>(s_cur[1][0]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (HP) ex_a(6 * KK + 2);
+        if constexpr (HP) ex_a_after(KK, 1);
         __builtin_amdgcn_sched_barrier(0);
         mfma_s<T, F, R, 1, 0, KK>(s_cur[0][1]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (HP) { ex_a(6 * KK + 3); ex_a(6 * KK + 4); }
+        if constexpr (HP) ex_a_after(KK, 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_s<T, F, R, 1, 1, KK>(s_cur[1][1]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (HP) ex_a(6 * KK + 5);
+        if constexpr (HP) ex_a_after(KK, 3);
         if constexpr (HP && KK == KT - 1) commit(pa, rs_a, p_prev);
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -413,7 +431,7 @@ fwd_wide_kernel(FwdParams p) {
     } else if constexpr (HP) {
       read_v(vst, ic<0>{});
 #pragma unroll
-      for (int i = 0; i < 48; ++i) ex_a(i);
+      for (int i = 0; i < 8 * EA; ++i) ex_a(i);
       commit(pa, rs_a, p_prev);
     }
 
@@ -433,8 +451,12 @@ fwd_wide_kernel(FwdParams p) {
           if constexpr (J == 4) { max_part(s_cur, 1, 2); max_part(s_cur, 1, 3); }
           if constexpr (J == 5) finish_max(1);
         }
-        if constexpr (CC == 2) ex1(pb, s_cur, 0, 0, J, rs_b, p_cur);
-        if constexpr (CC == 3) ex1(pb, s_cur, 1, 0, J, rs_b, p_cur);
+        if constexpr (HP && CC >= 1) {
+          // slot k = 8 (CC - 1) + J of 24 takes B's exponentials [lo, hi)
+          constexpr int K = 8 * (CC - 1) + J;
+#pragma unroll
+          for (int i = (8 * NBX * K) / 24; i < (8 * NBX * (K + 1)) / 24; ++i) ex_b(i);
+        }
         if constexpr (CC == 3 && J == 7) commit(pb, rs_b, p_cur);
       }
     };
@@ -489,9 +511,7 @@ fwd_wide_kernel(FwdParams p) {
       slot(ic<1>{}, ic<4>{});
       slot(ic<1>{}, ic<5>{});
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ex1(pb, s_cur, 0, 0, e, rs_b, p_cur);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ex1(pb, s_cur, 1, 0, e, rs_b, p_cur);
+      for (int i = 0; i < 8 * NBX; ++i) ex_b(i);
       commit(pb, rs_b, p_cur);
     }
     rs_pend[0] = rs_b[0];
