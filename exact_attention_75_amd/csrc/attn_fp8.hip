@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernel_common.h"
 #include "kernels.h"
 
@@ -170,11 +172,13 @@ hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
 // 128 keys), folded into the exp2 argument.  Probabilities are produced as
 // P' = 2^6 (sv_t / sv_max) exp2(c s - m), where sv_t is the tile's V block
 // scale and sv_max the largest V block scale of the (batch, KV head), and m
-// is a lazily updated running max: it moves only when some row's max
-// exceeds it by more than TAU = 2 (log2 units, wave-uniform decision), so
-// c s - m <= 2 and P' <= 2^8, inside the E4M3 range.  O then accumulates in
-// one unit (sv_max / 2^6) for all V blocks and is rescaled only when m
-// moves -- rarely after the first tiles.  The row sum is taken over the fp32
+// is a lazily updated running max.  No per-tile row max is taken: a tile's
+// P' are computed against the current m and their sum over the lane's 32
+// keys, which bounds each of them, is checked against PMAX = 448 (the
+// largest E4M3 value).  Only when some lane exceeds it (or m is not set yet)
+// does m move to the tile's row max, with O and l rescaled and the tile's
+// P' recomputed.  O then accumulates in one unit (sv_max / 2^6) for all V
+// blocks and is rescaled only when m moves -- rarely after the first tiles.  The row sum is taken over the fp32
 // values and converted to l's units with 2^-6 sv_max / sv_t per tile.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -200,8 +204,8 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int TILE = BN * KROW;       // 8 KiB, same for V^T (D * VROW)
   constexpr int LOADS = TILE / 16 / (NW * 64);   // DMA instructions per wave per tensor
   constexpr float NEG_INF = -__builtin_inff();
-  constexpr float TAU = 2.0f;           // lazy-max threshold, log2 units
-  constexpr float POFF = 8.0f - TAU;    // log2 of P' for a probability of 1 at the running max
+  constexpr float POFF = 6.0f;          // log2 of P' for a probability of 1 at the running max
+  constexpr float PMAX = 448.0f;        // bound on a lane's share of a tile's sum of P' (E4M3 max)
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];   // [K0 | K1 | V0 | V1]
 
   const int tid = threadIdx.x;
@@ -304,16 +308,23 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
 
-  issue(0, 0);
-  for (int t = 0; t < ntile; ++t) {
+  float msub = 0.f;
+  // One key tile: barrier, the next tile's copies, and -- for tiles this
+  // wave computes -- S, the probabilities, the sum check and PV.  STAGE is
+  // t % 2, a constant, so every LDS read is a per-lane base plus an
+  // immediate offset.
+  auto step = [&](int t, auto stage_tag) {
+    constexpr int STAGE = decltype(stage_tag)::value;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntile) issue(t + 1, (t + 1) & 1);
-    if (t >= n_w) continue;
-    const char* Ks = smem + (t & 1) * TILE;
-    const char* Vs = smem + (2 + (t & 1)) * TILE;
+    if (t + 1 < ntile) issue(t + 1, STAGE ^ 1);
+    if (t >= n_w) return;
+    const char* Ks = smem + STAGE * TILE;
+    const char* Vs = smem + (2 + STAGE) * TILE;
     const int j0 = t * BN;
-    const float c = cbase * ksc[j0 >> 7];
-    const float lv = log2f(vsc[j0 >> 7]) - lsv_max;   // <= 0
+    // block scales by scalar loads (a vector load would queue behind the
+    // copies in flight and make the tile wait for them)
+    const float c = cbase * ((const __attribute__((address_space(4))) float*)ksc)[j0 >> 7];
+    const float lv = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;   // <= 0
 
     // ---- S^T = K Q^T
     f32x16 s[2];
@@ -339,41 +350,49 @@ fwd_fp8_kernel(Fp8FwdParams p) {
           s[bb][i] = dead ? NEG_INF : s[bb][i];
         }
     }
-    // ---- lazy running max
-    float mx = NEG_INF;
+    // ---- P' = 2^(6 + lv) exp2(c s - m) -> E4M3 against the current max;
+    // row sum over the fp32 values
+    float rs;
+    i32x8 pk;
+    auto probs = [&]() {
+      const float off = POFF + lv - msub;
+      rs = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+      for (int w = 0; w < 8; ++w) {
+        float e[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
-    mx = fmaxf(mx, wave_half_swap(mx));
-    const float m_new = fmaxf(m_run, mx * c);
-    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0;
-    const float m_upd = moved ? m_new : m_run;
-    const float alpha = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
-    m_run = m_upd;
-    const float msub = (m_run == NEG_INF) ? 0.f : m_run;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-      asm volatile("" ::: "memory");   // keep the rare rescale a branch
+        for (int j = 0; j < 4; ++j) {
+          const int k = 4 * w + j;           // 0..31: block k / 16, element k % 16
+          e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k >> 4][k & 15], c, off));
+          rs += e[j];
+        }
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
+      }
+    };
+    probs();
+    // ---- the lane's sum bounds each of its probabilities: unless some
+    // lane's exceeds PMAX (or is not finite), or the row has no max yet, the
+    // tile is done.  Otherwise (rare) the max moves to the tile's row max, O
+    // and l are rescaled and the probabilities recomputed.
+    if (__builtin_amdgcn_ballot_w64(!(rs <= PMAX) || m_run == NEG_INF) != 0) {
+      asm volatile("" ::: "memory");   // keep the rare path a branch
+      float mx = NEG_INF;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
+      mx = fmaxf(mx, wave_half_swap(mx));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      msub = (m_run == NEG_INF) ? 0.f : m_run;
+      probs();
     }
-    // ---- P' = 2^(6 + lv) exp2(c s - m) -> E4M3; row sum over the fp32 values
-    const float off = POFF + lv - msub;
-    float rs = 0.f;
-    i32x8 pk;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 4 * w + j;           // 0..31: block k / 16, element k % 16
-        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k >> 4][k & 15], c, off));
-        rs += e[j];
-      }
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-      pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
-    }
-    l_run = l_run * alpha + rs * __builtin_amdgcn_exp2f(-POFF - lv);
+    l_run += rs * __builtin_amdgcn_exp2f(-POFF - lv);
     // ---- O^T += V^T P'^T
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -381,7 +400,16 @@ fwd_fp8_kernel(Fp8FwdParams p) {
       const i32x4 hi = *(const i32x4*)(Vs + voff2[db]);
       o[db] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
     }
+  };
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  issue(0, 0);
+  int t = 0;
+  for (; t + 2 <= ntile; t += 2) {
+    step(t, S0{});
+    step(t + 1, S1{});
   }
+  if (t < ntile) step(t, S0{});
 
   // ---- epilogue: O = O_acc sv_max / (2^6 l) (bf16), LSE = ln2 (m + log2 l)
   const float l_tot = l_run + wave_half_swap(l_run);

@@ -116,6 +116,36 @@ def test_fwd_fp8_kernel_vs_oracle(ea, causal, shape):
     assert err <= FP8_RELRMS
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_running_max_moves(ea, causal):
+    # channel 0 holds q = 1 and k = alpha * (128 * (j // 128)): the scores
+    # step up by `step` log2 units at each 128-key boundary, so the running
+    # max has to move again and again (causal rows within 32 keys of a step
+    # boundary see only a few keys of their top step and are left out)
+    B, S, Hq, Hkv = 1, 1104, 2, 1                 # the fp8 kernel needs Sk % 16 == 0
+    q, _, _ = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=33)
+    _, k, v = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=34)
+    scale = 1 / math.sqrt(128)
+    rows = np.arange(S)
+    if causal:
+        rows = rows[rows % 128 >= 32]
+    for step in (20.0, 60.0):
+        alpha = step / (scale * math.log2(math.e) * 128)
+        q2, k2 = q.clone(), k.clone()
+        q2[..., 0] = 1.0
+        k2[..., 0] = (alpha * 128 * (torch.arange(S, dtype=torch.float64) // 128)).view(1, S, 1).float()
+        print(f"[case] fwd_fp8 running max moves causal={causal} step={step}", flush=True)
+        O, L, (cq, sq, ck, sk, cv, sv) = oracle_fp8(q2, k2, v, causal, scale)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        o, lse = ea.fwd_fp8(t(cq), t(ck), t(np.transpose(cv, (0, 2, 3, 1))), t(sq), t(sk), t(sv), causal=causal)
+        torch.cuda.synchronize()
+        og = o.float().cpu().double().numpy()[:, rows]
+        err = relrms(og, O[:, rows])
+        lerr = float(np.abs(lse.cpu().double().numpy()[:, :, rows] - L[:, :, rows]).max())
+        print(f"[fp8] max moves step {step}: O rel-RMS {err:.3e}, LSE max-abs {lerr:.3e}")
+        assert err <= FP8_RELRMS
+
+
 @pytest.mark.parametrize("dtype", ["fp8", "fp8_hadamard"])
 def test_fwd_fp8_end_to_end(ea, dtype):
     B, S, H = 1, 512, 4
