@@ -286,25 +286,15 @@ fwd_wide_kernel(FwdParams p) {
   // barrier; the round's copies -- K_{r+STAGES-1} into the slot of K_{r-1},
   // V_{r+STAGES-2} into the slot of V_{r-2} -- go out one per k-step of the
   // iteration's first stretch.  Iteration r reads K_r and V_{r-1}.
-#ifndef ATTN_WIDE_PRE
-#define ATTN_WIDE_PRE 0
-#endif
-  // PRE: the K reads of k-steps 0 and 1 of tile t+1 are issued at the end of
-  // iteration t (its barrier then waits for one round of copies more, so
-  // that K_{t+1} is in LDS), and the next barrier lets those four reads stay
-  // in flight (LDS reads complete in order: every older read has landed)
-  constexpr int PRE = ATTN_WIDE_PRE;
-  auto top_wait = [&](auto lgkm_tag) {
-    constexpr int LG = decltype(lgkm_tag)::value;
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(2 * LOADS * (STAGES - 2 - PRE)), "n"(LG)
-                 : "memory");
+  auto top_wait = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS * (STAGES - 2)) : "memory");
   };
   auto round_copy = [&](const Copy& kc, const Copy& vc, int i) {
     if (i < LOADS) copy_row_to_lds(kc.src, kc.bytes, kc.dst + i * 1024, kdma[i]);
     else copy_row_to_lds(vc.src, vc.bytes, vc.dst + (i - LOADS) * 1024, vdma[i - LOADS]);
   };
   auto top = [&](int r) {
-    top_wait(ic<0>{});
+    top_wait();
     issue(Kp, r + STAGES - 1, kbuf(r + STAGES - 1), kdma);
     issue(Vp, r + STAGES - 2, vbuf(r + STAGES - 2), vdma);
   };
@@ -368,7 +358,7 @@ fwd_wide_kernel(FwdParams p) {
     // with S_t to compute, the round's copies go one per k-step of A
     Copy kc{}, vc{};
     if constexpr (HS) {
-      top_wait(ic<(PRE && HP) ? 4 : 0>{});
+      top_wait();
       kc = copy_of(Kp, t + STAGES - 1, kbuf(t + STAGES - 1));
       vc = copy_of(Vp, t + STAGES - 2, vbuf(t + STAGES - 2));
     } else {
@@ -398,10 +388,8 @@ fwd_wide_kernel(FwdParams p) {
 
     // ---- A: S_t = K_t Q^T, EA exponentials of S_{t-1} per k-step
     if constexpr (HS) {
-      if constexpr (!(PRE && HP)) {
-        read_k(kst, ic<0>{});
-        read_k(kst, ic<1>{});
-      }
+      read_k(kst, ic<0>{});
+      read_k(kst, ic<1>{});
       auto kstep = [&](auto kk_tag) {
         constexpr int KK = decltype(kk_tag)::value;
         constexpr int R = KK % 3;
@@ -528,11 +516,6 @@ fwd_wide_kernel(FwdParams p) {
     }
     rs_pend[0] = rs_b[0];
     rs_pend[1] = rs_b[1];
-    if constexpr (PRE && HS) {
-      const uint32_t kst_next = (uint32_t)(slot_of(t + 1) * TILE);
-      read_k(kst_next, ic<0>{});
-      read_k(kst_next, ic<1>{});
-    }
   };
 
   // ---------------------------------------------------------------- key loop
