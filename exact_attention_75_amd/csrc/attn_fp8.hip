@@ -53,6 +53,56 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tT[D][ROWS + 16];   // transposed codes
 
+  if (p.signs == nullptr && !p.transpose_out) {
+    // Row-major codes without rotation: no thread needs a whole row, so the
+    // lanes read coalesced -- in each load, lanes 0-31 read one 512-byte row
+    // and lanes 32-63 the next -- and write 128-byte rows of codes.  Wave w
+    // covers rows 32 w .. 32 w + 31, two per load.
+    const int lane = tid & 63, w = tid >> 6;
+    const int c4 = 4 * (lane & 31);       // first of the lane's 4 channels
+    float4 xv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int rr = 32 * w + 2 * k + (lane >> 5);
+      if (rr < nrows) {
+        const long long ri = ((long long)b * p.S + row0 + rr) * p.H + h;
+        xv[k] = *(const float4*)(p.x + ri * D + c4);
+      } else {
+        xv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      am = fmaxf(fmaxf(am, fmaxf(fabsf(xv[k].x), fabsf(xv[k].y))), fmaxf(fabsf(xv[k].z), fabsf(xv[k].w)));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) red[w] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = am > 0.f ? am / 448.0f : 1.0f;
+    if (tid == 0) p.descale[((long long)b * p.H + h) * nblk + blk] = s;
+    const float inv = 1.0f / s;
+    auto quant = [&](float v) {
+      // correctly rounded v / s (Markstein: q0 within one ulp, exact
+      // remainder, one correcting FMA), clipped
+      const float q0 = v * inv;
+      const float r = __builtin_fmaf(-q0, s, v);
+      return fminf(fmaxf(__builtin_fmaf(r, inv, q0), -448.0f), 448.0f);
+    };
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int rr = 32 * w + 2 * k + (lane >> 5);
+      int code = __builtin_amdgcn_cvt_pk_fp8_f32(quant(xv[k].x), quant(xv[k].y), 0, false);
+      code = __builtin_amdgcn_cvt_pk_fp8_f32(quant(xv[k].z), quant(xv[k].w), code, true);
+      if (rr < nrows) {
+        const long long ri = ((long long)b * p.S + row0 + rr) * p.H + h;
+        *(int*)(p.x8 + ri * D + c4) = code;
+      }
+    }
+    return;
+  }
+
   // ---- load the thread's 64 channels of its row
   float x[HALF];
   const long long rowidx = ((long long)b * p.S + row0 + r) * p.H + h;
@@ -107,13 +157,24 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
   const float s = am > 0.f ? am / 448.0f : 1.0f;
   if (tid == 0) p.descale[((long long)b * p.H + h) * nblk + blk] = s;
 
-  // ---- quantise: E4M3(clip(x / s)), round to nearest even
+  // ---- quantise: E4M3(clip(x / s)), round to nearest even.  x / s is the
+  // correctly rounded fp32 quotient, formed from the correctly rounded
+  // reciprocal: q0 = x * inv is within one ulp of x / s, the remainder
+  // x - q0 s is exact in one FMA, and one more FMA q0 + r inv rounds to the
+  // nearest quotient (Markstein's division theorem; a subnormal quotient may
+  // be one ulp off, which no E4M3 code resolves: they all map to zero)
+  const float inv = 1.0f / s;
+  auto divide = [&](float v) {
+    const float q0 = v * inv;
+    const float r = __builtin_fmaf(-q0, s, v);
+    return __builtin_fmaf(r, inv, q0);
+  };
   uint32_t q[HALF / 4];
 #pragma unroll
   for (int i = 0; i < HALF; i += 4) {
     float y[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(x[i + j] / s, -448.0f), 448.0f);
+    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(divide(x[i + j]), -448.0f), 448.0f);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
     q[i / 4] = (uint32_t)w;
