@@ -61,6 +61,37 @@ def test_prepass_exact_without_rotation(ea, shape):
     np.testing.assert_array_equal(sc_t.cpu().numpy(), rs)
 
 
+def test_prepass_exact_near_rounding_midpoints(ea):
+    # every block's amax is a chosen A (so s = A / 448 in fp32 on both sides)
+    # and the other values are placed within two fp32 ulps of x = mid * s,
+    # mid an E4M3 rounding midpoint: there any error in the fp32 quotient
+    # x / s changes the code
+    B, S, H, d = 1, 512, 2, 128
+    rng = np.random.default_rng(77)
+    mids = np.array([(1 + (m + 0.5) / 8) * 2.0 ** e for e in range(-6, 8) for m in range(8)]
+                    + [(m + 0.5) / 8 * 2.0 ** -6 for m in range(8)])
+    x = np.empty((B, S, H, d), dtype=np.float32)
+    for blk in range(S // 128):
+        for h in range(H):
+            A = np.float32(rng.uniform(0.01, 100.0))
+            s = A / np.float32(448.0)
+            m = rng.choice(mids, size=(128, d)) * rng.choice([-1.0, 1.0], size=(128, d))
+            v = (m * np.float64(s)).astype(np.float32)
+            steps = rng.integers(-2, 3, size=v.shape)
+            for k in (1, 2):
+                v = np.where(steps >= k, np.nextafter(v, np.float32(np.inf)), v)
+                v = np.where(steps <= -k, np.nextafter(v, np.float32(-np.inf)), v)
+            v[0, 0] = A
+            x[0, 128 * blk:128 * (blk + 1), h] = v
+    codes, sc = ea.fp8_prepass(torch.from_numpy(x).cuda())
+    codes_t, _ = ea.fp8_prepass(torch.from_numpy(x).cuda(), transpose_out=True)
+    torch.cuda.synchronize()
+    rc, rs = F.block_quantize(x)
+    np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(codes_t.cpu().numpy(), np.transpose(rc, (0, 2, 3, 1)))
+
+
 def test_prepass_rotation_within_one_code(ea):
     B, S, H = 1, 512, 4
     x, _, _ = fp32_inputs(B, S, H, 128, seed=22, outliers=True)
