@@ -1,6 +1,6 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--no-extra]
 
 One step is one pass of the hot path over one batch of the workload: for the
 bf16/fp16 workloads one ``attn_fwd`` call; for the fp8 workloads the fp8
@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--extra", action="store_true", help="also time the other workloads (stderr)")
+    ap.add_argument("--no-extra", action="store_true", help="skip timing the other 16-bit workloads (c1, c2, c4)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 workloads")
     ap.add_argument("--no-split", action="store_true", help="skip the split-KV decode leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
@@ -393,7 +393,7 @@ def main():
                              and not W.CONFIGS[a.workload].varlen else "c3", max(5, a.steps // 5), 3)
         if a.workload != "c4":
             out["bwd_varlen"] = bwd_leg(ea, "c4", max(5, a.steps // 5), 3)
-    if a.extra:
+    if not a.no_extra:
         for name in ("c1", "c2", "c4"):
             if name == a.workload:
                 continue
@@ -404,8 +404,12 @@ def main():
             msx = time_steps(sx, n, a.warmup) / n
             fx = flops_of(wx, dx["lengths"])
             print(f"[extra] {name} {msx * 1e3:.1f} us  {fx / (msx * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr)
-            out.setdefault("other_workloads", {})[name] = {"ms": round(msx, 5),
-                                                          "tflops": round(fx / (msx * 1e-3) / 1e12, 2)}
+            out.setdefault("other_workloads", {})[name] = {
+                "workload": f"{wx.name}: " + (f"varlen T={wx.Sq} tokens in {wx.B} sequences" if wx.varlen
+                                              else f"B={wx.B} S={wx.Sq}") +
+                            f" Hq={wx.Hq} Hkv={wx.Hkv} d={wx.d} {wx.dtype} {'causal' if wx.causal else 'full'}",
+                "ms": round(msx, 5), "tflops": round(fx / (msx * 1e-3) / 1e12, 2),
+                "pct_of_dense_mfma_peak": round(100 * fx / (msx * 1e-3) / 1e12 / PEAK_TFLOPS[wx.dtype], 2)}
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
     print(json.dumps(out), flush=True)
