@@ -113,9 +113,10 @@ def test_scale_other_than_default(ea):
     compare(o, lse, o_ref, l_ref, "scale 0.3")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_running_max_moves(ea, dtype, causal):
+def test_running_max_moves(ea, dtype, causal, d):
     # channel 0 holds q = 1 and k = alpha * (128 * (j // 128)): every row's
     # scores step up by `step` log2 units at each 128-key boundary, so the
     # running max has to move again and again, by more than any lazy
@@ -123,7 +124,7 @@ def test_running_max_moves(ea, dtype, causal):
     # Causal rows within 32 keys of a step boundary see only a few keys of
     # their top step, where bf16 rounding of P alone reaches the O gate:
     # those rows are left out of the comparison.
-    B, S, Hq, Hkv, d = 1, 1100, 4, 2, 128
+    B, S, Hq, Hkv = 1, 1100, 4, 2
     q, k, v = W.make_dense(B, S, S, Hq, Hkv, d, dtype, seed=12)
     scale = 1 / math.sqrt(d)
     rows = np.arange(S)
@@ -134,11 +135,11 @@ def test_running_max_moves(ea, dtype, causal):
         q2, k2 = q.clone(), k.clone()
         q2[..., 0] = 1.0
         k2[..., 0] = (alpha * 128 * (torch.arange(S, dtype=torch.float64) // 128)).view(1, S, 1).to(k.dtype)
-        print(f"[case] running max moves {dtype} causal={causal} step={step}", flush=True)
+        print(f"[case] running max moves {dtype} d={d} causal={causal} step={step}", flush=True)
         o, lse = run_dense(ea, q2, k2, v, causal)
         o_ref, l_ref = A.attention(q2, k2, v, scale, causal, rows=rows)
         compare(o[:, rows], lse[:, :, rows], o_ref[:, rows], l_ref[:, :, rows],
-                f"max moves {dtype} c{int(causal)} step {step}")
+                f"max moves {dtype} d{d} c{int(causal)} step {step}")
 
 
 def test_deterministic(ea):
