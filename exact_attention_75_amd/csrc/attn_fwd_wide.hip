@@ -21,10 +21,11 @@
 //    so the softmax of a tile runs under the matrix products of the two
 //    stretches around it (the pages' overlap of the GEMMs with the softmax,
 //    "flash-attention-3", "Why a schedule", within one instruction stream).
-//  * K and V tiles stream global -> LDS through double buffers of
-//    direct-to-LDS copies.  Every round issues the same copies (a copy past
-//    the last tile has an empty buffer range and writes zeros into a free
-//    buffer), so the loop has no branches around them.
+//  * K and V tiles stream global -> LDS through four-slot rings of
+//    direct-to-LDS copies, two tiles ahead, with one workgroup barrier per
+//    two key tiles.  Every round issues the same copies (a copy past the
+//    last tile has an empty buffer range and writes zeros into a free slot),
+//    so the loop has no branches around them.
 //  * The running max is exact after the first key tile and then moves only
 //    when a tile's probabilities, taken against the current max, sum to more
 //    than PMAX in some lane: the sum bounds every probability of the tile, so
@@ -281,22 +282,35 @@ fwd_wide_kernel(FwdParams p) {
     pd = Pend{x, qb, cc, e, true};
   };
 
-  // Round r: wait for the copies of round r-STAGES+1 and older (every round
-  // issues the same 2 LOADS copies, so STAGES-2 rounds stay in flight) and
-  // barrier; the round's copies -- K_{r+STAGES-1} into the slot of K_{r-1},
-  // V_{r+STAGES-2} into the slot of V_{r-2} -- go out one per k-step of the
-  // iteration's first stretch.  Iteration r reads K_r and V_{r-1}.
+  // Round r precedes iteration r, which reads K_r and V_{r-1}; the round's
+  // copies go out one per k-step of the iteration's first stretch.  Without
+  // BAR2: every round waits for the copies of round r-STAGES+1 and older
+  // (every round issues the same 2 LOADS copies, so STAGES-2 rounds stay in
+  // flight) and barriers, then copies K_{r+STAGES-1} into the slot of
+  // K_{r-1} and V_{r+STAGES-2} into the slot of V_{r-2}.
+#ifndef ATTN_WIDE_BAR2
+#define ATTN_WIDE_BAR2 1
+#endif
+  // BAR2: one barrier per two iterations.  Iteration r copies K_{r+2} and
+  // V_{r+1}; the barrier of an even iteration r waits for all of the wave's
+  // copies (K_r, K_{r+1}, V_{r-1}, V_r), and every slot written until the
+  // next barrier (those of K_{r-2}, K_{r-1}, V_{r-3}, V_{r-2}) was last read
+  // before this one.
+  constexpr bool BAR2 = ATTN_WIDE_BAR2;
+  constexpr int KLA = BAR2 ? 2 : STAGES - 1;   // K tile copied by round r: r + KLA
+  constexpr int VLA = BAR2 ? 1 : STAGES - 2;   // V tile copied by round r: r + VLA
   auto top_wait = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS * (STAGES - 2)) : "memory");
+    if constexpr (BAR2) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS * (STAGES - 2)) : "memory");
   };
   auto round_copy = [&](const Copy& kc, const Copy& vc, int i) {
     if (i < LOADS) copy_row_to_lds(kc.src, kc.bytes, kc.dst + i * 1024, kdma[i]);
     else copy_row_to_lds(vc.src, vc.bytes, vc.dst + (i - LOADS) * 1024, vdma[i - LOADS]);
   };
   auto top = [&](int r) {
-    top_wait();
-    issue(Kp, r + STAGES - 1, kbuf(r + STAGES - 1), kdma);
-    issue(Vp, r + STAGES - 2, vbuf(r + STAGES - 2), vdma);
+    if (!BAR2 || (r & 1) == 0) top_wait();
+    issue(Kp, r + KLA, kbuf(r + KLA), kdma);
+    issue(Vp, r + VLA, vbuf(r + VLA), vdma);
   };
 
   // One iteration.  HS: S_t is computed (t < n_w); HP: tile
@@ -358,9 +372,9 @@ fwd_wide_kernel(FwdParams p) {
     // with S_t to compute, the round's copies go one per k-step of A
     Copy kc{}, vc{};
     if constexpr (HS) {
-      top_wait();
-      kc = copy_of(Kp, t + STAGES - 1, kbuf(t + STAGES - 1));
-      vc = copy_of(Vp, t + STAGES - 2, vbuf(t + STAGES - 2));
+      if (!BAR2 || (t & 1) == 0) top_wait();
+      kc = copy_of(Kp, t + KLA, kbuf(t + KLA));
+      vc = copy_of(Vp, t + VLA, vbuf(t + VLA));
     } else {
       top(t);
     }
@@ -525,9 +539,9 @@ fwd_wide_kernel(FwdParams p) {
   // empty copy, so that every round issues the same number of copies) ..
   // V_{STAGES-3}
 #pragma unroll
-  for (int r = -STAGES + 1; r < 0; ++r) {
-    issue(Kp, r + STAGES - 1, kbuf(r + STAGES - 1), kdma);
-    issue(Vp, r + STAGES - 2 >= 0 ? r + STAGES - 2 : ntile, vbuf(r + STAGES - 2), vdma);
+  for (int r = -KLA; r < 0; ++r) {
+    issue(Kp, r + KLA, kbuf(r + KLA), kdma);
+    issue(Vp, r + VLA >= 0 ? r + VLA : ntile, vbuf(r + VLA), vdma);
   }
   f32x16 s0[QB][NB], s1[QB][NB];
   vec8 p0[QB][NC], p1[QB][NC];
