@@ -535,9 +535,9 @@ fwd_wide_kernel(FwdParams p) {
   // ---------------------------------------------------------------- key loop
   // Iterations 0 .. n_w: S_t (t < n_w) and P_{t-1} V_{t-1} (t >= 1).  Even
   // iterations keep tile t in s0 / p0, odd ones in s1 / p1.
-  // prologue rounds -STAGES+1 .. -1: K_0 .. K_{STAGES-2} and V_{-1} (an
-  // empty copy, so that every round issues the same number of copies) ..
-  // V_{STAGES-3}
+  // prologue rounds -KLA .. -1: K_0 .. K_{KLA-1} and V_{VLA-KLA} .. V_{VLA-1}
+  // (a V tile before the first is an empty copy, so that every round issues
+  // the same number of copies)
 #pragma unroll
   for (int r = -KLA; r < 0; ++r) {
     issue(Kp, r + KLA, kbuf(r + KLA), kdma);
