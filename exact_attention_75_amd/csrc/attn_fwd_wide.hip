@@ -49,7 +49,12 @@ using namespace wide;
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <typename T, bool CAUSAL>
+// H4 (grouped-query attention with a group of 4k heads): the workgroup owns
+// 64 query rows of four query heads of one KV head, one head per wave, and
+// p.tm runs over (batch, head quadruple, 64-row block).  All four waves then
+// see the same keys, so a causal workgroup has no waves idling past their
+// diagonal while the last one finishes.
+template <typename T, bool CAUSAL, bool H4>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_wide_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -92,6 +97,7 @@ fwd_wide_kernel(FwdParams p) {
 
   int b, hq, mblk;
   tile_decode(p.tm, blockIdx.x, b, hq, mblk);
+  if constexpr (H4) hq = 4 * hq + wave;
   const int q_len = p.Sq, kv_len = p.Sk;
   const int hkv = hq / p.group;
   const T* Qp = (const T*)p.q + (long long)b * p.q_batch_stride + hq * D;
@@ -102,9 +108,10 @@ fwd_wide_kernel(FwdParams p) {
   const int qs = p.q_tok_stride;
   const int ks = p.kv_tok_stride;
 
-  const int q0 = mblk * BM;
-  const int qw = q0 + 64 * wave;                         // first query row of this wave
-  const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;
+  constexpr int ROWS = H4 ? 64 : BM;                    // query rows per head of the workgroup
+  const int q0 = mblk * ROWS;
+  const int qw = H4 ? q0 : q0 + 64 * wave;              // first query row of this wave
+  const int q_hi = q0 + ROWS < q_len ? q0 + ROWS : q_len;
   const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
   const int ntile = (kv_end + BN - 1) / BN;
   // key tiles this wave computes: up to its diagonal when causal, none when
@@ -605,19 +612,35 @@ fwd_wide_kernel(FwdParams p) {
   }
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool H4>
 static hipError_t launch_wide_one(const FwdParams& p, hipStream_t s) {
   constexpr int lds = 2 * ATTN_WIDE_STAGES * 64 * 128 * 2;   // K and V rings of 16 KiB tiles
-  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_wide_kernel<T, CAUSAL>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_wide_kernel<T, CAUSAL, H4>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fwd_wide_kernel<T, CAUSAL>), dim3(p.grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((fwd_wide_kernel<T, CAUSAL, H4>), dim3(p.grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
+#ifndef ATTN_WIDE_HEADS4
+#define ATTN_WIDE_HEADS4 1
+#endif
+
+template <typename T>
+static hipError_t launch_wide_t(const FwdParams& p, int causal, hipStream_t s) {
+  if (ATTN_WIDE_HEADS4 && p.group % 4 == 0) {
+    // four query heads of one KV head per workgroup, 64 rows each
+    FwdParams q = p;
+    q.tm = make_tile_map(p.B, p.Hq / 4, p.Hkv, p.Sq, 64, causal);
+    q.grid = q.tm.ntiles;
+    return causal ? launch_wide_one<T, true, true>(q, s) : launch_wide_one<T, false, true>(q, s);
+  }
+  return causal ? launch_wide_one<T, true, false>(p, s) : launch_wide_one<T, false, false>(p, s);
+}
+
 hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s) {
-  if (dtype == 0) return causal ? launch_wide_one<__bf16, true>(p, s) : launch_wide_one<__bf16, false>(p, s);
-  return causal ? launch_wide_one<_Float16, true>(p, s) : launch_wide_one<_Float16, false>(p, s);
+  if (dtype == 0) return launch_wide_t<__bf16>(p, causal, s);
+  return launch_wide_t<_Float16>(p, causal, s);
 }
 
 }  // namespace attn
