@@ -324,7 +324,7 @@ fwd_wide_kernel(FwdParams p) {
   // t-1 is finished and P_{t-1} V_{t-1} added (t >= 1).  s_cur / p_cur
   // receive tile t, s_prev / p_prev hold tile t-1.
   float rs_a[QB] = {0.f, 0.f};     // sums of P_{t-1} computed in A
-  float rs_pend[QB] = {0.f, 0.f};  // sums of chunk 0 of the tile computed in the previous B
+  float rs_pend[QB] = {0.f, 0.f};  // sums of the tile's first NBX groups, computed in the previous B
   // Tile t-1 is complete (all its probabilities taken against msub): l takes
   // its sum, unless some lane's share exceeds PMAX (or is not finite).  Then
   // the running max moves to the tile's row max, O and l are rescaled, and
