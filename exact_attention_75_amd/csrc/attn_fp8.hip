@@ -391,8 +391,13 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     const float c = cbase * ((const __attribute__((address_space(4))) float*)ksc)[j0 >> 7];
     const float lv = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;   // <= 0
 
-    // ---- S^T = K Q^T
+    // ---- S^T = K Q^T.  Each MFMA group runs at raised wave priority: the
+    // other wave on this SIMD (another workgroup's) is then mostly in its
+    // softmax, and its vector instructions fill the cycles of these MFMAs
+    // instead of holding them back (at equal priority the older wave wins
+    // the issue arbitration whatever it issues).
     f32x16 s[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       s[bb] = f32x16{};
@@ -403,6 +408,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
         s[bb] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf[kk], s[bb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- mask: element i of block bb is key j0 + 32 h + 16 bb + i
     const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
     if (edge) {
@@ -459,12 +465,14 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     }
     l_run += rs * __builtin_amdgcn_exp2f(-POFF - lv);
     // ---- O^T += V^T P'^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const i32x4 lo = *(const i32x4*)(Vs + voff[db]);
       const i32x4 hi = *(const i32x4*)(Vs + voff2[db]);
       o[db] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   typedef std::integral_constant<int, 0> S0;
   typedef std::integral_constant<int, 1> S1;
