@@ -237,7 +237,7 @@ hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
 // P' are computed against the current m and their sum over the lane's 32
 // keys, which bounds each of them, is checked against PMAX = 448 (the
 // largest E4M3 value).  Only when some lane exceeds it (or m is not set yet)
-// does m move to the tile's row max, with O and l rescaled and the tile's
+// does m move to 4 above the tile's row max, with O and l rescaled and the tile's
 // P' recomputed.  O then accumulates in one unit (sv_max / 2^4) for all V
 // blocks and is rescaled only when m moves -- rarely after the first tiles.  The row sum is taken over the fp32
 // values and converted to l's units with 2^-4 sv_max / sv_t per tile.  The
@@ -454,7 +454,11 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[bb][i]);
       mx = fmaxf(mx, wave_half_swap(mx));
-      const float m_new = fmaxf(m_run, mx * c);
+      // the new max sits 4 (log2 units) above the tile's row max: a max that
+      // creeps up over the next tiles then stays within the bound instead of
+      // taking this branch again (P' at the row max is 2^0 instead of 2^4;
+      // the reference point cancels in O and l either way)
+      const float m_new = fmaxf(m_run, mx * c + 4.f);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
