@@ -75,6 +75,8 @@ def library() -> ctypes.CDLL:
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_release.argtypes = []
     L.attn_release.restype = None
+    L.attn_test_fail_next.argtypes = [I]
+    L.attn_test_fail_next.restype = I
     _lib = L
     return L
 

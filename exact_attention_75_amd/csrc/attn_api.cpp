@@ -36,10 +36,26 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
   return ATTN_OK;
 }
 
+// --- failure injection (attn_test_fail_next): one armed code per thread --
+thread_local int g_fail_next = 0;
+
+// A launch is about to be enqueued: hipSuccess, or the simulated launch
+// failure that attn_test_fail_next(ATTN_ERR_HIP) armed (then nothing runs).
+hipError_t launch_gate() {
+  if (g_fail_next != ATTN_ERR_HIP) return hipSuccess;
+  g_fail_next = 0;
+  return hipErrorLaunchFailure;
+}
+
 // --- workspaces: lazily grown device buffers, one per (use, device) -------
 // kWsFp8 holds the quantised operands of attn_fwd's fp8 types, kWsSplit the
 // split-KV partials, kWsBwd the backward's per-row statistics; separate
-// buffers, so the paths never share memory.
+// buffers, so the paths never share memory.  Growth is stream-ordered: the
+// old buffer is released with hipFreeAsync on the calling stream (after the
+// work already queued there) and the new one taken with hipMallocAsync, so
+// no call waits for the device.  Work queued on another stream that still
+// uses the old buffer is not waited for: calls that share a workspace on
+// different streams must not overlap (the header states it).
 constexpr int kMaxDevices = 64;
 enum { kWsFp8 = 0, kWsSplit = 1, kWsBwd = 2, kWsKinds = 3 };
 struct Workspace {
@@ -49,7 +65,11 @@ struct Workspace {
 Workspace g_ws[kWsKinds][kMaxDevices];
 std::mutex g_ws_mu;
 
-int workspace(int kind, size_t bytes, void** out) {
+int workspace(int kind, size_t bytes, hipStream_t s, void** out) {
+  if (g_fail_next == ATTN_ERR_NOMEM) {
+    g_fail_next = 0;
+    return ATTN_ERR_NOMEM;
+  }
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -58,17 +78,16 @@ int workspace(int kind, size_t bytes, void** out) {
   Workspace& w = g_ws[kind][dev];
   if (w.bytes < bytes) {
     if (w.ptr) {
-      // the old buffer may still be in use by enqueued work
-      e = hipDeviceSynchronize();
+      e = hipFreeAsync(w.ptr, s);
       if (e != hipSuccess) return hip_fail(e);
-      (void)hipFree(w.ptr);
       w.ptr = nullptr;
       w.bytes = 0;
     }
-    e = hipMalloc(&w.ptr, bytes);
+    e = hipMallocAsync(&w.ptr, bytes, s);
     if (e != hipSuccess) {
       w.ptr = nullptr;
-      return ATTN_ERR_NOMEM;
+      (void)hipGetLastError();
+      return e == hipErrorOutOfMemory ? ATTN_ERR_NOMEM : hip_fail(e);
     }
     w.bytes = bytes;
   }
@@ -142,16 +161,6 @@ int split_plan(long long tiles, int Sk, int d, int num_splits, int* splits, int*
   return ATTN_OK;
 }
 
-uint64_t splitmix64(uint64_t x) {
-  uint64_t z = x * 0x9E3779B97F4A7C15ULL;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-  return z ^ (z >> 31);
-}
-
-// device copy of the default sign vector, per device
-float* g_signs[kMaxDevices] = {};
-
 void fill_params(attn::FwdParams& p, const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int Sq, int Sk, int d, float scale) {
   p.q = q;
@@ -186,21 +195,23 @@ int fwd16_dense(const void* q, const void* k, const void* v, void* o, float* lse
   p.tm = pack ? attn::make_tile_map(B, Hkv, Hkv, Sq * g, bm, causal) : attn::make_tile_map(B, Hq, Hkv, Sq, bm, causal);
   if (splits <= 1) {
     p.grid = p.tm.ntiles;
-    hipError_t e = attn::launch_fwd(p, dtype, d, causal, 0, s);
+    hipError_t e = launch_gate();
+    if (e == hipSuccess) e = attn::launch_fwd(p, dtype, d, causal, 0, s);
     return e == hipSuccess ? ATTN_OK : hip_fail(e);
   }
   const size_t rows = (size_t)B * Sq * Hq;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t ob = al(sizeof(float) * splits * rows * d), lb = al(sizeof(float) * splits * rows);
   void* ws = nullptr;
-  int rc = workspace(kWsSplit, ob + lb, &ws);
+  int rc = workspace(kWsSplit, ob + lb, s, &ws);
   if (rc) return rc;
   p.splits = splits;
   p.split_keys = split_keys;
   p.o_part = (float*)ws;
   p.lse_part = (float*)((uint8_t*)ws + ob);
   p.grid = p.tm.ntiles * splits;
-  hipError_t e = attn::launch_fwd_split(p, dtype, d, causal, s);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_fwd_split(p, dtype, d, causal, s);
   if (e != hipSuccess) return hip_fail(e);
   return attn_combine(p.o_part, p.lse_part, o, lse, splits, B, Hq, Sq, d, dtype, s);
 }
@@ -228,8 +239,7 @@ const char* attn_strerror(int code) {
 int attn_default_signs(float* signs_host, int n) {
   if (!signs_host) return ATTN_ERR_NULL;
   if (n <= 0 || n > 128) return ATTN_ERR_SHAPE;
-  for (int i = 0; i < n; ++i)
-    signs_host[i] = (splitmix64((55ULL << 32) + (uint64_t)i + 1) >> 63) ? -1.f : 1.f;
+  for (int i = 0; i < n; ++i) signs_host[i] = attn::default_sign(i);
   return ATTN_OK;
 }
 
@@ -279,7 +289,8 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   p.scale_log2 = scale * 1.4426950408889634f;
   p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_fp8_block_m(), causal);
   p.grid = p.tm.ntiles;
-  hipError_t e = attn::launch_fwd_fp8(p, causal, (hipStream_t)stream);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_fwd_fp8(p, causal, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -294,12 +305,14 @@ int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, 
   p.x8 = x8;
   p.descale = descale;
   p.signs = signs;
+  p.default_signs = 0;
   p.B = B;
   p.S = S;
   p.H = H;
   p.d = d;
   p.transpose_out = transpose_out ? 1 : 0;
-  hipError_t e = attn::launch_prepass(p, (hipStream_t)stream);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_prepass(p, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -327,7 +340,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     const size_t sq_b = al(sizeof(float) * B * Hq * nbq), sk_b = al(sizeof(float) * B * Hkv * nbk);
     const size_t total = al(qb) + 2 * al(kb) + sq_b + 2 * sk_b;
     void* ws = nullptr;
-    rc = workspace(kWsFp8, total, &ws);
+    rc = workspace(kWsFp8, total, s, &ws);
     if (rc) return rc;
     uint8_t* base = (uint8_t*)ws;
     uint8_t* q8 = base;
@@ -336,31 +349,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     float* qs = (float*)(v8t + al(kb));
     float* ks = (float*)((uint8_t*)qs + sq_b);
     float* vs = (float*)((uint8_t*)ks + sk_b);
-    const float* sg = nullptr;
-    if (dtype == ATTN_FP8_E4M3_HADAMARD) {
-      int dev = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e != hipSuccess) return hip_fail(e);
-      if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_ARG;
-      std::lock_guard<std::mutex> lk(g_ws_mu);
-      if (!g_signs[dev]) {
-        float hs[128];
-        attn_default_signs(hs, 128);
-        float* dp = nullptr;
-        e = hipMalloc(&dp, sizeof hs);
-        if (e != hipSuccess) return ATTN_ERR_NOMEM;
-        e = hipMemcpy(dp, hs, sizeof hs, hipMemcpyHostToDevice);
-        if (e != hipSuccess) {
-          (void)hipFree(dp);
-          return hip_fail(e);
-        }
-        g_signs[dev] = dp;
-      }
-      sg = g_signs[dev];
-    }
-    rc = attn_fp8_prepass((const float*)q, q8, qs, B, Sq, Hq, d, 0, sg, stream);
-    if (!rc) rc = attn_fp8_prepass((const float*)k, k8, ks, B, Sk, Hkv, d, 0, sg, stream);
-    if (!rc) rc = attn_fp8_prepass((const float*)v, v8t, vs, B, Sk, Hkv, d, 1, nullptr, stream);
+    // the Hadamard type rotates Q and K with the default signs, which the
+    // prepass kernel holds in constant memory
+    auto prepass = [&](const float* x, uint8_t* x8, float* ds, int S, int H, int transpose, int rotate) {
+      attn::PrepassParams pp{};
+      pp.x = x;
+      pp.x8 = x8;
+      pp.descale = ds;
+      pp.signs = nullptr;
+      pp.default_signs = rotate;
+      pp.B = B;
+      pp.S = S;
+      pp.H = H;
+      pp.d = d;
+      pp.transpose_out = transpose;
+      hipError_t e = launch_gate();
+      if (e == hipSuccess) e = attn::launch_prepass(pp, s);
+      return e == hipSuccess ? ATTN_OK : hip_fail(e);
+    };
+    const int rot = dtype == ATTN_FP8_E4M3_HADAMARD ? 1 : 0;
+    rc = prepass((const float*)q, q8, qs, Sq, Hq, 0, rot);
+    if (!rc) rc = prepass((const float*)k, k8, ks, Sk, Hkv, 0, rot);
+    if (!rc) rc = prepass((const float*)v, v8t, vs, Sk, Hkv, 1, 0);
     if (!rc) rc = attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream);
     return rc;
   }
@@ -380,7 +390,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const long long nb = (Sq + bm - 1) / bm + B;
   if (nb * Hq > kMax32) return ATTN_ERR_SIZE;
   p.grid = (int)(nb * Hq);
-  hipError_t e = attn::launch_fwd(p, dtype, d, causal, 1, s);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_fwd(p, dtype, d, causal, 1, s);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -413,7 +424,8 @@ int attn_combine(const float* o_part, const float* lse_part, void* o, float* lse
   p.Hq = Hq;
   p.Sq = Sq;
   p.d = d;
-  hipError_t e = attn::launch_combine(p, dtype, (hipStream_t)stream);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_combine(p, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -455,7 +467,8 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
   }
   p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal);
   p.grid = p.tm.ntiles;
-  hipError_t e = attn::launch_fwd(p, dtype, d, causal, 0, (hipStream_t)stream);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_fwd(p, dtype, d, causal, 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
@@ -479,7 +492,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if ((long long)Hkv * nkb > kMax32 || (long long)Hq * nqb > kMax32) return ATTN_ERR_SIZE;
   const int sq_pad = varlen ? Sq : (Sq + 31) / 32 * 32;
   void* ws = nullptr;
-  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)(varlen ? 1 : B) * Hq * sq_pad, &ws);
+  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)(varlen ? 1 : B) * Hq * sq_pad, (hipStream_t)stream, &ws);
   if (rc) return rc;
   attn::BwdParams p{};
   p.q = q;
@@ -510,8 +523,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     p.grid_dq = p.tm.ntiles;
   }
   p.grid_dkdv = (int)(Hkv * nkb);
-  hipError_t e = attn::launch_bwd(p, dtype, d, causal, varlen ? 1 : 0, (hipStream_t)stream);
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_bwd(p, dtype, d, causal, varlen ? 1 : 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_test_fail_next(int code) {
+  if (code != 0 && code != ATTN_ERR_NOMEM && code != ATTN_ERR_HIP) return ATTN_ERR_ARG;
+  g_fail_next = code;
+  return ATTN_OK;
 }
 
 void attn_release(void) {
@@ -519,17 +539,16 @@ void attn_release(void) {
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return;
   for (int dev = 0; dev < kMaxDevices; ++dev) {
-    bool any = g_signs[dev] != nullptr;
+    bool any = false;
     for (int k = 0; k < kWsKinds; ++k) any = any || g_ws[k][dev].ptr != nullptr;
     if (!any) continue;
     if (hipSetDevice(dev) != hipSuccess) continue;
     (void)hipDeviceSynchronize();
     for (int k = 0; k < kWsKinds; ++k) {
-      if (g_ws[k][dev].ptr) (void)hipFree(g_ws[k][dev].ptr);
+      if (g_ws[k][dev].ptr) (void)hipFreeAsync(g_ws[k][dev].ptr, nullptr);
       g_ws[k][dev] = Workspace{};
     }
-    if (g_signs[dev]) (void)hipFree(g_signs[dev]);
-    g_signs[dev] = nullptr;
+    (void)hipDeviceSynchronize();
   }
   (void)hipSetDevice(cur);
 }

@@ -38,6 +38,19 @@ __device__ __forceinline__ float lane_xor1(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
+// The default sign vector, generated at compile time: the rotation of
+// attn_fwd's Hadamard type reads it from constant memory, so no call has to
+// copy it to the device first.
+struct SignTable {
+  float v[128];
+};
+constexpr SignTable make_default_signs() {
+  SignTable t{};
+  for (int i = 0; i < 128; ++i) t.v[i] = default_sign(i);
+  return t;
+}
+__constant__ SignTable kDefaultSigns = make_default_signs();
+
 __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
   constexpr int ROWS = 128, D = 128, HALF = 64;
   const int nblk = (p.S + ROWS - 1) / ROWS;
@@ -53,7 +66,8 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tT[D][ROWS + 16];   // transposed codes
 
-  if (p.signs == nullptr && !p.transpose_out) {
+  const float* signs = p.default_signs ? kDefaultSigns.v : p.signs;
+  if (signs == nullptr && !p.transpose_out) {
     // Row-major codes without rotation: no thread needs a whole row, so the
     // lanes read coalesced -- in each load, lanes 0-31 read one 512-byte row
     // and lanes 32-63 the next -- and write 128-byte rows of codes.  Wave w
@@ -122,9 +136,9 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
   }
 
   // ---- optional rotation: x <- (x * signs) H_128 / sqrt(128), in fp32
-  if (p.signs != nullptr) {
+  if (signs != nullptr) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) x[i] *= p.signs[half * HALF + i];
+    for (int i = 0; i < HALF; ++i) x[i] *= signs[half * HALF + i];
 #pragma unroll
     for (int len = 1; len < HALF; len <<= 1)
 #pragma unroll
@@ -230,27 +244,37 @@ hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
 // 32-byte LDS reads.
 //
 // Scales: scores are sq * sk_t * (Q~ K~^T) (sq per 128 query rows, sk_t per
-// 128 keys), folded into the exp2 argument.  Probabilities are produced as
-// P' = 2^4 (sv_t / sv_max) exp2(c s - m), where sv_t is the tile's V block
-// scale and sv_max the largest V block scale of the (batch, KV head), and m
-// is a lazily updated running max.  No per-tile row max is taken: a tile's
-// P' are computed against the current m and their sum over the lane's 32
-// keys, which bounds each of them, is checked against PMAX = 448 (the
-// largest E4M3 value).  Only when some lane exceeds it (or m is not set yet)
-// does m move to 4 above the tile's row max, with O and l rescaled and the tile's
-// P' recomputed.  O then accumulates in one unit (sv_max / 2^4) for all V
-// blocks and is rescaled only when m moves -- rarely after the first tiles.  The row sum is taken over the fp32
-// values and converted to l's units with 2^-4 sv_max / sv_t per tile.  The
-// factor 2^4 keeps a lane's sum of 32 P' well under 448 when the max is
-// current (a factor 2^6 put the typical sum near 300 on N(0,1) scores, and
-// the rare path ran on a large share of the tiles), while P' of a
-// probability 2^-10 is still a normal E4M3 value.
+// 128 keys), folded into the exp2 argument.  O accumulates in one unit for
+// every V block: sv_ref / 2^4, sv_ref the largest V block scale among the
+// blocks the workgroup's rows can see.  The ratio sv_t / sv_ref of the
+// tile's V block (log2 lv <= 0) is split as lv = e + f with the integer
+// e = ceil(lv) <= 0 and f in (-1, 0]: 2^e is the MFMA's E8M0 scale of the
+// V operand (exact, any size), and only 2^f enters the probabilities,
+// P' = 2^(4 + f) exp2(c s - m), m a lazily updated running max.  So P' does
+// not shrink with the V block ratio: a block whose scale is far below the
+// largest keeps its probabilities in the normal E4M3 range (folding the
+// whole ratio into P' sent them to subnormals or zero, and rows that see
+// only such blocks lost their output).
+// No per-tile row max is taken: a tile's P' are computed against the
+// current m and their sum over the lane's 32 keys, which bounds each of
+// them, is checked against PMAX = 448 (the largest E4M3 value).  Only when
+// some lane exceeds it (or m is not set yet) does m move to 4 above the
+// tile's row max, with O and l rescaled and the tile's P' recomputed; O is
+// otherwise never rescaled.  The row sum is taken over the fp32 values and
+// converted to l's units with 2^(-4 - f) per tile.  The factor 2^4 keeps a
+// lane's sum of 32 P' well under 448 when the max is current (a factor 2^6
+// put the typical sum near 300 on N(0,1) scores, and the rare path ran on a
+// large share of the tiles).
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// the same product with the A operand scaled by 2^(a_scale - 127) (E8M0)
+__device__ __forceinline__ f32x16 mma_fp8_sa(const i32x8& a, const i32x8& b, const f32x16& c, int a_scale) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, a_scale, 0, 127);
 }
 
 // K tile row r (128 bytes = 8 chunks): chunk c stored at c ^ swz_k8(r)
@@ -291,16 +315,17 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   const float* ksc = p.k_descale + ((long long)b * p.Hkv + hkv) * nbk;
   const float* vsc = p.v_descale + ((long long)b * p.Hkv + hkv) * nbk;
   const float sq = p.q_descale[((long long)b * p.Hq + hq) * nbq + mblk];
-  // largest V block scale of this (batch, KV head) (uniform loads)
-  float sv_max = 0.f;
-  for (int i = 0; i < nbk; ++i) sv_max = fmaxf(sv_max, vsc[i]);
-  const float lsv_max = log2f(sv_max);
 
   const int q0 = mblk * BM;
   const int qw = q0 + wave * 32;
   const int q_hi = q0 + BM < q_len ? q0 + BM : q_len;
   const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
   const int ntile = (kv_end + BN - 1) / BN;
+  // O's unit: the largest V block scale among the blocks these rows see
+  // (uniform loads)
+  float sv_max = 0.f;
+  for (int i = 0; i < (kv_end + 127) / 128; ++i) sv_max = fmaxf(sv_max, vsc[i]);
+  const float lsv_max = log2f(sv_max);
   const int qi = qw + l32;
 
   // Q fragment: lane holds query qi, channels 64 kk + 32 h .. +31
@@ -389,7 +414,11 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     // block scales by scalar loads (a vector load would queue behind the
     // copies in flight and make the tile wait for them)
     const float c = cbase * ((const __attribute__((address_space(4))) float*)ksc)[j0 >> 7];
-    const float lv = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;   // <= 0
+    // V block ratio 2^lv = 2^(e + f): 2^e as the E8M0 scale of V (clamped at
+    // the format's 2^-127), 2^f in P'
+    const float lv_all = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;
+    const int vscale = max(0, 127 + (int)ceilf(lv_all));
+    const float lv = lv_all - (float)(vscale - 127);   // (-1, 0] unless clamped
 
     // ---- S^T = K Q^T.  Each MFMA group runs at raised wave priority: the
     // other wave on this SIMD (another workgroup's) is then mostly in its
@@ -421,8 +450,8 @@ fwd_fp8_kernel(Fp8FwdParams p) {
           s[bb][i] = dead ? NEG_INF : s[bb][i];
         }
     }
-    // ---- P' = 2^(6 + lv) exp2(c s - m) -> E4M3 against the current max;
-    // row sum over the fp32 values
+    // ---- P' = 2^(4 + f) exp2(c s - m) -> E4M3 against the current max (lv
+    // holds f); row sum over the fp32 values
     float rs;
     i32x8 pk;
     auto probs = [&]() {
@@ -474,7 +503,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     for (int db = 0; db < 4; ++db) {
       const i32x4 lo = *(const i32x4*)(Vs + voff[db]);
       const i32x4 hi = *(const i32x4*)(Vs + voff2[db]);
-      o[db] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
+      o[db] = mma_fp8_sa(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db], vscale);
     }
     __builtin_amdgcn_s_setprio(0);
   };

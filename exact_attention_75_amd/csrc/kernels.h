@@ -98,10 +98,25 @@ struct PrepassParams {
   const float* x;             // [B, S, H, d]
   uint8_t* x8;                // [B, S, H, d] or [B, H, d, S]
   float* descale;             // [B, H, ceil(S/128)]
-  const float* signs;         // d signs or nullptr
+  const float* signs;         // d signs (device) or nullptr
+  int default_signs;          // non-zero: rotate with the built-in default signs (signs ignored)
   int B, S, H, d;
   int transpose_out;
 };
+
+// splitmix64 (Steele, Lea, Flood 2014): the output for counter value x
+// (state x * golden gamma, then the published mixing constants)
+constexpr uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x * 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+// Default sign i of the Hadamard rotation: the top bit of
+// splitmix64((55 << 32) + i + 1) gives -1, else +1.
+constexpr float default_sign(int i) {
+  return (splitmix64((55ULL << 32) + (uint64_t)i + 1) >> 63) ? -1.f : 1.f;
+}
 
 // Query rows per workgroup of the bf16/fp16 forward for this configuration.
 int fwd_block_m(int dtype, int d, int varlen);

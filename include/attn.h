@@ -18,7 +18,17 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call is asynchronous: it validates its arguments on the host,
  *     enqueues kernels on `stream` and returns; results are ready after the
- *     stream is synchronised.  No call blocks or copies host<->device.
+ *     stream is synchronised.  No call blocks or copies host<->device
+ *     (attn_release, which frees the workspaces, is the one call that waits
+ *     for the device).
+ *   - Library-owned workspaces (the fp8 operands of attn_fwd's fp8 types,
+ *     the split-KV partials, the backward's row statistics; one buffer per
+ *     use and device) grow stream-ordered: a call that needs a larger buffer
+ *     frees the old one with hipFreeAsync on its own stream (after the work
+ *     queued there) and allocates the new one with hipMallocAsync.  So calls
+ *     that use the same workspace from different streams of one device, or
+ *     from several host threads, must not overlap: the caller orders them
+ *     (one stream, or events between the streams).
  *   - Return value 0 (ATTN_OK) on success, a negative ATTN_ERR_* code on
  *     failure.  Validation happens before anything is enqueued, so a call
  *     that returns an error has written nothing.  Nothing throws or aborts
@@ -92,8 +102,10 @@ enum attn_status {
  *   attn_fwd_splitkv); the result does not depend on that choice.
  * dtype: an attn_dtype.  For the fp8 types q, k, v are fp32 and o is bf16;
  *   the quantised copies live in a library-owned, lazily grown device
- *   workspace (released by attn_release); the Hadamard variant uses the
- *   library's default sign vector (attn_default_signs).  fp8 needs d == 128
+ *   workspace (released by attn_release; fp8 calls on different streams of
+ *   one device share it and must not overlap); the Hadamard variant uses the
+ *   library's default sign vector (attn_default_signs), compiled into the
+ *   library's device code.  fp8 needs d == 128
  *   and Sk a multiple of 16, and no cu_seqlens.
  * lse may be NULL when the caller does not want it.
  */
@@ -287,8 +299,19 @@ int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* 
 const char* attn_strerror(int code);
 
 /* Frees the library's workspaces (fp8 operands, split-KV partials, backward
- * statistics) on every device that has them. */
+ * statistics) on every device that has them.  Waits for each such device to
+ * finish its queued work first (hipDeviceSynchronize). */
 void attn_release(void);
+
+/* Failure injection for tests of the error paths (the failures a host-only
+ * test cannot otherwise produce).  Arms a one-shot failure for the calling
+ * thread: after attn_test_fail_next(ATTN_ERR_NOMEM) the next workspace
+ * allocation fails as if the device were out of memory (the call returns
+ * ATTN_ERR_NOMEM); after attn_test_fail_next(ATTN_ERR_HIP) the next kernel
+ * launch reports a launch failure instead of running (ATTN_ERR_HIP, with the
+ * text in attn_strerror).  Either way nothing is enqueued.  0 disarms.
+ * Returns ATTN_OK, or ATTN_ERR_ARG for any other code. */
+int attn_test_fail_next(int code);
 
 #ifdef __cplusplus
 }

@@ -209,3 +209,80 @@ def test_fwd_ext_validates(lib):
     assert fx(d=96) == -3 and fx(Hq=3) == -4
     # both options off: plain attn_fwd validation
     assert fx(cap=0.0, Sq=0) == -2
+
+
+# ---------------------------------------------------------------- failure paths
+# attn_test_fail_next arms a one-shot failure that fires before anything is
+# enqueued, so these calls (with pointers that are never dereferenced) are
+# safe with or without a GPU.
+NOMEM, HIPERR = -7, -8
+
+
+def splitkv(lib, **kw):
+    a = dict(B=1, Hq=2, Hkv=2, Sq=256, Sk=4096, d=128, splits=4, pack=0, dtype=0)
+    a.update(kw)
+    return lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"],
+                                0.1, 0, a["splits"], a["pack"], a["dtype"], None)
+
+
+def bwd(lib):
+    return lib.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 2, 2, 256, 256, 64, 0.125,
+                        0, None, 0, None)
+
+
+@pytest.mark.parametrize("call", ["fwd_fp8_type", "fwd_fp8_hadamard", "splitkv", "bwd"])
+def test_workspace_allocation_failure(lib, call):
+    # every path that takes a library workspace reports ATTN_ERR_NOMEM when
+    # the allocation fails
+    assert lib.attn_test_fail_next(NOMEM) == 0
+    if call == "fwd_fp8_type":
+        rc = fwd(lib, dtype=2, d=128)
+    elif call == "fwd_fp8_hadamard":
+        rc = fwd(lib, dtype=3, d=128)
+    elif call == "splitkv":
+        rc = splitkv(lib)
+    else:
+        rc = bwd(lib)
+    assert rc == NOMEM
+    assert lib.attn_strerror(rc) == b"device workspace allocation failed"
+
+
+@pytest.mark.parametrize("call", ["fwd_dense", "fwd_varlen", "fwd_ext", "fwd_fp8", "prepass", "combine"])
+def test_launch_failure(lib, call):
+    # a launch that fails maps to ATTN_ERR_HIP with the runtime's text
+    assert lib.attn_test_fail_next(HIPERR) == 0
+    if call == "fwd_dense":
+        rc = fwd(lib)
+    elif call == "fwd_varlen":
+        rc = fwd(lib, cu=FAKE, B=3, Sq=512, Sk=512)
+    elif call == "fwd_ext":
+        rc = lib.attn_fwd_ext(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 2, 256, 256, 128, 0.1, 0, None, 0, 30.0, 0, None)
+    elif call == "fwd_fp8":
+        rc = lib.attn_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 1, 128, 128, 128, 0.1, 0, None)
+    elif call == "prepass":
+        rc = lib.attn_fp8_prepass(FAKE, FAKE, FAKE, 1, 128, 1, 128, 0, None, None)
+    else:
+        rc = lib.attn_combine(FAKE, FAKE, FAKE, None, 4, 1, 2, 16, 128, 0, None)
+    assert rc == HIPERR
+    msg = lib.attn_strerror(rc).decode()
+    assert msg.startswith("HIP error") and "launch" in msg.lower(), msg
+
+
+def test_failure_hook_is_one_shot_and_validated(lib):
+    assert lib.attn_test_fail_next(-3) == -6          # only NOMEM, HIP or 0
+    assert lib.attn_test_fail_next(HIPERR) == 0
+    assert lib.attn_test_fail_next(0) == 0            # disarmed
+    # validation still comes first: an armed failure is not consumed by a
+    # call that fails validation
+    assert lib.attn_test_fail_next(NOMEM) == 0
+    assert fwd(lib, dtype=2, d=64) == -3
+    assert fwd(lib, dtype=2, d=128) == NOMEM
+    assert lib.attn_test_fail_next(0) == 0
+
+
+def test_every_status_code_is_covered():
+    # the error codes the header declares, each exercised above or in
+    # test_validation_errors / test_other_entry_points_validate
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"(ATTN_ERR_\w+)\s*=\s*(-\d+)", src))
+    assert set(codes.values()) == {-1, -2, -3, -4, -5, -6, -7, -8, -9}

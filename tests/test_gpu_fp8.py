@@ -10,7 +10,9 @@
   inputs the kernel consumes (the oracle's own quantisation of the same fp32
   inputs), relative RMS <= 5e-2.  The end-to-end error against the unquantised
   inputs is reported, not gated (it is a property of the format, not of the
-  kernel).
+  kernel).  The LSE comes from exact fp8 products accumulated in fp32 and a
+  row sum over fp32 probabilities, so it is gated like the 16-bit paths'
+  (max-abs <= 1e-3) against the same oracle.
 """
 import math
 
@@ -18,12 +20,14 @@ import numpy as np
 import pytest
 import torch
 
+import rounding_bounds as RB
 import workloads as W
 from oracle import attention as A
 from oracle import fp8 as F
 
 pytestmark = pytest.mark.gpu
 FP8_RELRMS = 5e-2
+FP8_LSE = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -145,21 +149,65 @@ def test_fwd_fp8_kernel_vs_oracle(ea, causal, shape):
     lerr = float(np.abs(lse.cpu().double().numpy() - L).max())
     print(f"[fp8] kernel vs oracle-on-dequantised: O rel-RMS {err:.3e}, LSE max-abs {lerr:.3e}")
     assert err <= FP8_RELRMS
+    check_lse(lse, L, cq, sq, ck, sk, scale, causal, None, f"fp8 {shape} c{int(causal)}", flat=FP8_LSE)
+
+
+def dequantised(cq, sq, ck, sk, cv, sv):
+    return F.dequantize(cq, sq), F.dequantize(ck, sk), F.dequantize(cv, sv)
+
+
+def check_lse(lse_gpu, L, cq, sq, ck, sk, scale, causal, rows, tag, flat=None, heads=None, batches=None):
+    """LSE of the selected rows within the bound derived from the fp8 MFMA's
+    summation (tests/rounding_bounds.py: max_j |dS_ij| plus the fp32 terms),
+    and within `flat` (the 16-bit paths' 1e-3) where that is asked for.
+    Returns the per-row score-error bound for check_bound."""
+    rows = np.arange(L.shape[2]) if rows is None else np.asarray(rows)
+    delta, eps = RB.fp8_score_error(cq, sq, ck, sk, scale, causal, rows, heads, batches)
+    lg = lse_gpu.cpu().double().numpy()[:, :, rows]
+    lr = L[:, :, rows]
+    sel = ~np.isnan(lr)
+    if heads is not None or batches is not None:
+        keep = np.zeros(lr.shape, dtype=bool)
+        for b in (range(lr.shape[0]) if batches is None else batches):
+            for h in (range(lr.shape[1]) if heads is None else heads):
+                keep[b, h] = True
+        sel &= keep
+    err = np.abs(lg - lr)
+    ratio = float((err[sel] / (delta + eps)[sel]).max())
+    print(f"[lse] {tag}: LSE max-abs {err[sel].max():.3e}, max error / derived bound {ratio:.3f} "
+          f"(bound up to {(delta + eps)[sel].max():.3e})", flush=True)
+    assert ratio <= 1.0, (tag, ratio)
+    if flat is not None:
+        assert err[sel].max() <= flat, (tag, err[sel].max())
+    return delta
+
+
+def check_bound(og, dq, dk, dv, scale, causal, rows, tag, score_err=None):
+    """Every element of og (rows `rows`) within the rounding bound of the fp8
+    path (tests/rounding_bounds.py, E4M3 probabilities, bf16 output)."""
+    bound, o_ref = RB.rounding_bound(dq, dk, dv, scale, causal, "fp8", rows, score_err)
+    err = np.abs(og - o_ref)
+    ratio = float((err / bound).max())
+    print(f"[bound] {tag}: max error / derived bound {ratio:.3f}", flush=True)
+    assert ratio <= 1.0, (tag, ratio)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_fp8_running_max_moves(ea, causal):
     # channel 0 holds q = 1 and k = alpha * (128 * (j // 128)): the scores
     # step up by `step` log2 units at each 128-key boundary, so the running
-    # max has to move again and again (causal rows within 32 keys of a step
-    # boundary see only a few keys of their top step and are left out)
+    # max has to move again and again.  Causal rows within 32 keys past a
+    # step boundary see only a few keys of their top step, where the E4M3
+    # rounding of the probabilities is not averaged away: those rows are
+    # gated by the bound derived from that rounding, the others by the
+    # rel-RMS gate, and the LSE of every row by the LSE gate.
     B, S, Hq, Hkv = 1, 1104, 2, 1                 # the fp8 kernel needs Sk % 16 == 0
     q, _, _ = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=33)
     _, k, v = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=34)
     scale = 1 / math.sqrt(128)
     rows = np.arange(S)
-    if causal:
-        rows = rows[rows % 128 >= 32]
+    few = rows[rows % 128 < 32] if causal else rows[:0]
+    many = np.setdiff1d(rows, few)
     for step in (20.0, 60.0):
         alpha = step / (scale * math.log2(math.e) * 128)
         q2, k2 = q.clone(), k.clone()
@@ -170,11 +218,68 @@ def test_fwd_fp8_running_max_moves(ea, causal):
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         o, lse = ea.fwd_fp8(t(cq), t(ck), t(np.transpose(cv, (0, 2, 3, 1))), t(sq), t(sk), t(sv), causal=causal)
         torch.cuda.synchronize()
-        og = o.float().cpu().double().numpy()[:, rows]
-        err = relrms(og, O[:, rows])
-        lerr = float(np.abs(lse.cpu().double().numpy()[:, :, rows] - L[:, :, rows]).max())
+        og = o.float().cpu().double().numpy()
+        err = relrms(og[:, many], O[:, many])
+        lerr = float(np.abs(lse.cpu().double().numpy() - L).max())
         print(f"[fp8] max moves step {step}: O rel-RMS {err:.3e}, LSE max-abs {lerr:.3e}")
         assert err <= FP8_RELRMS
+        delta = check_lse(lse, L, cq, sq, ck, sk, scale, causal, None, f"fp8 max moves c{int(causal)} step {step}")
+        if len(few):
+            check_bound(og[:, few], *dequantised(cq, sq, ck, sk, cv, sv), scale, causal, few,
+                        f"fp8 max moves c{int(causal)} step {step} few-key rows", score_err=delta[:, :, few])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", ["late_large", "span"])
+def test_fwd_fp8_v_block_scales(ea, causal, case):
+    # V block scales far apart within one head.  late_large: the 128-token
+    # block 6 of V is scaled by 2^12; with the mask, rows before it see only
+    # blocks 2^12 below the head's largest, and without it the block's keys
+    # get scores 30 log2 units below the rest, so every row's output is
+    # carried by the small blocks.  span: block b scaled by 2^(-12 b / 8)
+    # plus one block scaled by 2^8 late in the sequence.  Gates: rel-RMS over
+    # all rows, rel-RMS over the rows that see only small-scale blocks as a
+    # set of their own, the LSE gate, and the derived rounding bound per
+    # element (a lost V block ratio -- probabilities that underflow -- breaks
+    # all of them).
+    B, S, Hq, Hkv = 1, 1152, 2, 1
+    q, _, _ = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=36)
+    _, k, v = W.make_dense(B, S, S, Hq, Hkv, 128, "fp8", seed=37)
+    scale = 1 / math.sqrt(128)
+    nb = S // 128
+    fac = np.ones(nb)
+    if case == "late_large":
+        fac[6] = 2.0 ** 12
+    else:
+        fac = 2.0 ** (-12.0 * np.arange(nb) / 8)
+        fac[7] = 2.0 ** 8
+    v = v * torch.from_numpy(np.repeat(fac, 128)).float().view(1, S, 1, 1)
+    q2, k2 = q.clone(), k.clone()
+    if case == "late_large" and not causal:
+        alpha = 30.0 / (scale * math.log2(math.e))
+        q2[..., 0] = 1.0
+        k2[:, 768:896, :, 0] = -alpha
+    print(f"[case] fwd_fp8 V block scales {case} causal={causal}", flush=True)
+    O, L, (cq, sq, ck, sk, cv, sv) = oracle_fp8(q2, k2, v, causal, scale)
+    print(f"[fp8] V block scales (log2): {np.round(np.log2(sv[0, 0]), 2).tolist()}", flush=True)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o, lse = ea.fwd_fp8(t(cq), t(ck), t(np.transpose(cv, (0, 2, 3, 1))), t(sq), t(sk), t(sv), causal=causal)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    err = relrms(og, O)
+    lerr = float(np.abs(lse.cpu().double().numpy() - L).max())
+    if causal:
+        small = np.arange(768) if case == "late_large" else np.arange(896)   # rows before the large block
+    else:
+        small = np.arange(S)
+    err_small = relrms(og[:, small], O[:, small])
+    print(f"[fp8] V block scales {case} c{int(causal)}: O rel-RMS {err:.3e}, small-block rows {err_small:.3e}, "
+          f"LSE max-abs {lerr:.3e}", flush=True)
+    assert err <= FP8_RELRMS
+    assert err_small <= FP8_RELRMS
+    delta = check_lse(lse, L, cq, sq, ck, sk, scale, causal, None, f"fp8 V block scales {case} c{int(causal)}")
+    check_bound(og, *dequantised(cq, sq, ck, sk, cv, sv), scale, causal, None, f"fp8 V block scales {case}",
+                score_err=delta)
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "fp8_hadamard"])
@@ -183,15 +288,18 @@ def test_fwd_fp8_end_to_end(ea, dtype):
     q, k, v = fp32_inputs(B, S, H, 128, seed=41, outliers=True)
     scale = 1 / math.sqrt(128)
     signs = np.asarray(ea.default_signs(), dtype=np.float32) if dtype == "fp8_hadamard" else None
-    O, L, _ = oracle_fp8(q, k, v, False, scale, signs)
+    O, L, (cq, sq, ck, sk, _, _) = oracle_fp8(q, k, v, False, scale, signs)
     o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), dtype=dtype)
     torch.cuda.synchronize()
     og = o.float().cpu().double().numpy()
     err = relrms(og, O)
     exact, _ = A.attention(q, k, v, scale, False)
     e2e = relrms(og, exact)
-    print(f"[fp8] {dtype}: vs oracle-on-dequantised {err:.3e}; vs unquantised inputs {e2e:.3e} (reported)")
+    lerr = float(np.abs(lse.cpu().double().numpy() - L).max())
+    print(f"[fp8] {dtype}: vs oracle-on-dequantised {err:.3e} (LSE {lerr:.3e}); vs unquantised inputs {e2e:.3e} "
+          f"(reported)")
     assert err <= FP8_RELRMS
+    check_lse(lse, L, cq, sq, ck, sk, scale, False, None, f"fp8 end to end {dtype}")
 
 
 def test_c5_sampled(ea):
@@ -213,11 +321,57 @@ def test_c5_sampled(ea):
         ck, sk = F.block_quantize(kn)
         cv, sv = F.block_quantize(vn)
         dq, dk, dv = F.dequantize(cq, sq), F.dequantize(ck, sk), F.dequantize(cv, sv)
-        O, _ = A.attention(dq, dk, dv, w.scale, False, rows=rows)
+        O, L = A.attention(dq, dk, dv, w.scale, False, rows=rows)
         og = o.float().cpu().double().numpy()
         m = ~np.isnan(O)
         err = float(np.sqrt(((og[m] - O[m]) ** 2).sum() / (O[m] ** 2).sum()))
+        lm = ~np.isnan(L)
+        lerr = float(np.abs(lse.cpu().double().numpy()[lm] - L[lm]).max())
+        check_lse(lse, L, cq, sq, ck, sk, w.scale, False, rows, f"c5 {dtype}")
         Ox, _ = A.attention(q, k, v, w.scale, False, rows=rows)
         e2e = float(np.sqrt(((og[m] - Ox[m]) ** 2).sum() / (Ox[m] ** 2).sum()))
-        print(f"[fp8] c5 {dtype}: vs oracle-on-dequantised {err:.3e}; vs unquantised inputs {e2e:.3e}")
+        print(f"[fp8] c5 {dtype}: vs oracle-on-dequantised {err:.3e} (LSE {lerr:.3e}); "
+              f"vs unquantised inputs {e2e:.3e}")
         assert err <= FP8_RELRMS
+
+
+def test_c3fp8_sampled(ea):
+    """c3's shape in fp8 (B2 Hq32 Hkv8 S8192 causal, N(0,1) fp32 inputs), the
+    configuration the fp8 throughput is quoted on, at full size and in the
+    launch configuration the benchmark times (XCD-affine causal tile order):
+    sampled rows -- first and last query blocks, tile edges, random rows --
+    of a head of every KV group and both batches, through attn_fwd (library
+    prepass) and through attn_fwd_fp8 on the oracle's own codes, against the
+    oracle on the dequantised inputs.  The two entry points must agree bit for
+    bit (the prepass codes equal the oracle's without rotation)."""
+    w = W.CONFIGS["c3fp8"]
+    inp = W.make_inputs(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    S = w.Sq
+    rng = np.random.default_rng(35)
+    rows = np.array(sorted(set([0, 1, 31, 32, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 65, S - 33,
+                                S - 2, S - 1] + rng.integers(0, S, 12).tolist())))
+    group = w.Hq // w.Hkv
+    heads = sorted(set([0, w.Hq - 1] + [g * group + (g % group) for g in range(w.Hkv)]))
+    print(f"[case] c3fp8 full size: heads {heads}, {len(rows)} rows per head", flush=True)
+    o1, l1 = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, dtype="fp8")
+    cq, sq = F.block_quantize(q.numpy())
+    ck, sk = F.block_quantize(k.numpy())
+    cv, sv = F.block_quantize(v.numpy())
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o2, l2 = ea.fwd_fp8(t(cq), t(ck), t(np.transpose(cv, (0, 2, 3, 1))), t(sq), t(sk), t(sv), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    dq, dk, dv = dequantised(cq, sq, ck, sk, cv, sv)
+    og = o1.float().cpu().double().numpy()
+    lg = l1.cpu().double().numpy()
+    for b in range(w.B):
+        O, L = A.attention(dq, dk, dv, w.scale, True, heads=heads, rows=rows, batches=[b])
+        m = ~np.isnan(O[b])
+        err = float(np.sqrt(((og[b][m] - O[b][m]) ** 2).sum() / (O[b][m] ** 2).sum()))
+        lm = ~np.isnan(L[b])
+        lerr = float(np.abs(lg[b][lm] - L[b][lm]).max())
+        print(f"[fp8] c3fp8 b{b}: O rel-RMS {err:.3e}, LSE max-abs {lerr:.3e}", flush=True)
+        assert err <= FP8_RELRMS
+        check_lse(l1, L, cq, sq, ck, sk, w.scale, True, rows, f"c3fp8 b{b}", flat=FP8_LSE, heads=heads,
+                  batches=[b])

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import rounding_bounds as RB
 import workloads as W
 from oracle import attention as A
 
@@ -46,6 +47,17 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, tag=""):
     assert maxabs <= O_MAXABS, (tag, maxabs)
     assert relrms <= O_RELRMS, (tag, relrms)
     assert lmax <= LSE_ABS, (tag, lmax)
+
+
+def check_bound(o_gpu, q, k, v, scale, causal, kind, rows, tag):
+    """Every element of o_gpu (rows `rows` of a dense output) within the
+    rounding bound of tests/rounding_bounds.py."""
+    bound, o_ref = RB.rounding_bound(q, k, v, scale, causal, kind, rows)
+    og = o_gpu.detach().float().cpu().double().numpy()
+    err = np.abs(og - o_ref)
+    ratio = float((err / bound).max())
+    print(f"[bound] {tag}: max error / derived bound {ratio:.3f} (max-abs {err.max():.3e})", flush=True)
+    assert ratio <= 1.0, (tag, ratio)
 
 
 def run_dense(ea, q, k, v, causal, scale=None):
@@ -94,6 +106,38 @@ def test_single_key_and_identical_rows_exact(ea):
         assert torch.equal(o.cpu(), v[:, :1].expand(1, 300, 2, 64))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("path", ["wide", "wide_h4", "packgqa", "splitkv"])
+def test_identical_v_rows(ea, dtype, causal, path):
+    # identical V rows: the exact output is that row.  The kernels divide
+    # sum_j Pt_j v by l = sum_j P_j (P rounded to the operand type only for
+    # the product, l over the fp32 values), so O = v (sum Pt / sum P) before
+    # the output rounding: the derived rounding bound, which for identical
+    # rows is (u_P + eps) |v| + u_O |O| (plus the fp16 subnormal term).
+    # wide: the one-wave-per-SIMD d = 128 kernel, one head per tile; wide_h4:
+    # the same kernel with four query heads of a KV head per workgroup;
+    # packgqa: rows of all heads of a KV group in one 128-row tile (4-wave
+    # kernel); splitkv: key ranges and their combine.
+    Hq, Hkv = (2, 2) if path == "wide" else (8, 2)
+    Sq, Sk = (300, 700) if path in ("packgqa", "splitkv") else (700, 700)
+    q, k, v = W.make_dense(1, Sq, Sk, Hq, Hkv, 128, dtype, seed=14)
+    v = v[:, :1].expand(1, Sk, Hkv, 128).contiguous()
+    scale = 1 / math.sqrt(128)
+    print(f"[case] identical V rows {dtype} causal={causal} path={path}", flush=True)
+    if path == "packgqa":
+        o, lse = ea.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=1, pack_gqa=True)
+    elif path == "splitkv":
+        o, lse = ea.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=causal, num_splits=4, pack_gqa=False)
+    else:
+        o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    want = v[:, :1].repeat_interleave(Hq // Hkv, dim=2).expand(1, Sq, Hq, 128)
+    exact = float((o.cpu() == want).float().mean())
+    print(f"[exact] identical V rows {dtype} c{int(causal)} {path}: {exact * 100:.2f}% of elements equal v", flush=True)
+    check_bound(o, q, k, v, scale, causal, dtype, None, f"identical V rows {dtype} c{int(causal)} {path}")
+
+
 def test_zero_q_gives_log_n(ea):
     q = torch.zeros(1, 300, 2, 128, dtype=torch.bfloat16)
     _, k, v = W.make_dense(1, 300, 300, 2, 2, 128, "bf16", seed=5)
@@ -121,15 +165,18 @@ def test_running_max_moves(ea, dtype, causal, d):
     # scores step up by `step` log2 units at each 128-key boundary, so the
     # running max has to move again and again, by more than any lazy
     # threshold, while a row still averages the many keys of its last step.
-    # Causal rows within 32 keys of a step boundary see only a few keys of
-    # their top step, where bf16 rounding of P alone reaches the O gate:
-    # those rows are left out of the comparison.
+    # Causal rows within 32 keys past a step boundary see only a few keys of
+    # their top step: there the output is a mix of a handful of V rows and
+    # the rounding of P to the operand type is not averaged away, so those
+    # rows are gated by the bound derived from that rounding
+    # (tests/rounding_bounds.py), the others by the standard gate; the LSE
+    # gate holds for every row.
     B, S, Hq, Hkv = 1, 1100, 8, 2       # a group of 4: at d = 128 the head-packed wide kernel
     q, k, v = W.make_dense(B, S, S, Hq, Hkv, d, dtype, seed=12)
     scale = 1 / math.sqrt(d)
     rows = np.arange(S)
-    if causal:
-        rows = rows[rows % 128 >= 32]
+    few = rows[rows % 128 < 32] if causal else rows[:0]
+    many = np.setdiff1d(rows, few)
     for step in (20.0, 60.0):
         alpha = step / (scale * math.log2(math.e) * 128)
         q2, k2 = q.clone(), k.clone()
@@ -137,9 +184,14 @@ def test_running_max_moves(ea, dtype, causal, d):
         k2[..., 0] = (alpha * 128 * (torch.arange(S, dtype=torch.float64) // 128)).view(1, S, 1).to(k.dtype)
         print(f"[case] running max moves {dtype} d={d} causal={causal} step={step}", flush=True)
         o, lse = run_dense(ea, q2, k2, v, causal)
-        o_ref, l_ref = A.attention(q2, k2, v, scale, causal, rows=rows)
-        compare(o[:, rows], lse[:, :, rows], o_ref[:, rows], l_ref[:, :, rows],
+        o_ref, l_ref = A.attention(q2, k2, v, scale, causal)
+        compare(o[:, many], lse[:, :, many], o_ref[:, many], l_ref[:, :, many],
                 f"max moves {dtype} d{d} c{int(causal)} step {step}")
+        if len(few):
+            check_bound(o[:, few], q2, k2, v, scale, causal, dtype, few,
+                        f"max moves {dtype} d{d} c{int(causal)} step {step} few-key rows")
+            lg = lse.cpu().double().numpy()[:, :, few]
+            assert float(np.abs(lg - l_ref[:, :, few]).max()) <= LSE_ABS
 
 
 def test_deterministic(ea):

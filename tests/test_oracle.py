@@ -231,3 +231,28 @@ def test_flop_count():
     assert A.attention_flops(4, 4, 2, True) == 4 * 2 * 10
     assert A.attention_flops(8192, 8192, 128, True, B=2, H=32) == 4 * 128 * 64 * 8192 * 8193 // 2
     assert A.attention_flops(0, 0, 64, True, H=16, lengths=[3, 2]) == 4 * 64 * 16 * (6 + 3)
+
+
+def test_row_chunking_does_not_change_the_result():
+    # the forward oracle cuts a head's rows into chunks (1024 by default) to
+    # bound memory; chunks of 7 (ragged last chunk), 1024 (two chunks) and one
+    # chunk for all rows must give the same result, causal and not, also for
+    # a row subset that straddles chunk boundaries
+    q, k, v = rand(1100, 8), rand(1100, 8), rand(1100, 8)
+    for causal in (False, True):
+        Oc, Lc = A.head_attention(q, k, v, 0.4, causal, row_chunk=1100)
+        for chunk in (7, 1024):
+            O, L = A.head_attention(q, k, v, 0.4, causal, row_chunk=chunk)
+            np.testing.assert_allclose(O, Oc, rtol=1e-13, atol=1e-14)
+            np.testing.assert_allclose(L, Lc, rtol=1e-13, atol=1e-14)
+        rows = np.array([0, 6, 7, 8, 1023, 1024, 1099])
+        O, L = A.head_attention(q, k, v, 0.4, causal, rows=rows, row_chunk=7)
+        np.testing.assert_allclose(O, Oc[rows], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(L, Lc[rows], rtol=1e-13, atol=1e-14)
+    # and through the dense entry, whose heads are longer than one chunk
+    qd, kd, vd = rand(1, 1100, 2, 8), rand(1, 1100, 1, 8), rand(1, 1100, 1, 8)
+    Od, Ld = A.attention(qd, kd, vd, 0.4, True)
+    for h in range(2):
+        Oh, Lh = A.head_attention(qd[0, :, h], kd[0, :, 0], vd[0, :, 0], 0.4, True, row_chunk=1100)
+        np.testing.assert_allclose(Od[0, :, h], Oh, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(Ld[0, h], Lh, rtol=1e-13, atol=1e-14)
