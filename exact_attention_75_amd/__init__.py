@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "combine", "split_plan", "library",
+__all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "fwd_splitkv_noalloc", "combine", "split_plan", "library",
            "default_signs", "tile_of",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
@@ -63,6 +63,8 @@ def library() -> ctypes.CDLL:
     L.attn_grid_size.restype = I
     L.attn_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, I, P]
     L.attn_fwd_splitkv.restype = I
+    L.attn_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, I, P]
+    L.attn_fwd_splitkv_noalloc.restype = I
     L.attn_split_plan.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
     L.attn_split_plan.restype = I
     L.attn_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
@@ -216,6 +218,27 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
                                     float(scale), int(bool(causal)), int(num_splits), _pack_arg(pack_gqa), dt,
                                     _stream())
     _check(rc, "attn_fwd_splitkv")
+    return o, lse
+
+
+def fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                        scale: Optional[float] = None, num_splits: int = 0, pack_gqa: Optional[bool] = None,
+                        return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``fwd_splitkv`` through ``attn_fwd_splitkv_noalloc``: the library
+    allocates nothing (its partials use a fixed 16 MiB device array); o and
+    lse are allocated here, by torch, as for every entry point."""
+    _need_gpu(q, k, v)
+    dt = _kernel_dtype(q, k, v)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = library().attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                                            float(scale), int(bool(causal)), int(num_splits), _pack_arg(pack_gqa),
+                                            dt, _stream())
+    _check(rc, "attn_fwd_splitkv_noalloc")
     return o, lse
 
 

@@ -182,11 +182,46 @@ void fill_params(attn::FwdParams& p, const void* q, const void* k, const void* v
   p.scale_log2 = scale * 1.4426950408889634f;
 }
 
+// Bytes of split-KV partials for `rows` query rows: O_p then LSE_p, each
+// 256-byte aligned.
+size_t split_partials_bytes(int splits, size_t rows, int d, size_t* o_bytes) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  *o_bytes = al(sizeof(float) * splits * rows * d);
+  return *o_bytes + al(sizeof(float) * splits * rows);
+}
+
+// --- the fixed scratch of attn_fwd_splitkv_noalloc ------------------------
+// A file-scope device array: every GPU the library runs on holds its own
+// copy for the life of the process.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address is
+// taken once per device with hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+
 // Dense bf16/fp16 forward after validation: the plain kernels (splits == 1)
-// or split-KV partials and their combine, with or without PackGQA.
+// or split-KV partials and their combine, with or without PackGQA.  The
+// partials go to `fixed` when it is given (it holds at least their bytes),
+// else to the lazily grown workspace.
 int fwd16_dense(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
                 int Sk, int d, float scale, int causal, int pack, int splits, int split_keys, int dtype,
-                hipStream_t s) {
+                hipStream_t s, void* fixed = nullptr) {
   attn::FwdParams p{};
   fill_params(p, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale);
   p.pack = pack;
@@ -199,12 +234,13 @@ int fwd16_dense(const void* q, const void* k, const void* v, void* o, float* lse
     if (e == hipSuccess) e = attn::launch_fwd(p, dtype, d, causal, 0, s);
     return e == hipSuccess ? ATTN_OK : hip_fail(e);
   }
-  const size_t rows = (size_t)B * Sq * Hq;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t ob = al(sizeof(float) * splits * rows * d), lb = al(sizeof(float) * splits * rows);
-  void* ws = nullptr;
-  int rc = workspace(kWsSplit, ob + lb, s, &ws);
-  if (rc) return rc;
+  size_t ob = 0;
+  const size_t bytes = split_partials_bytes(splits, (size_t)B * Sq * Hq, d, &ob);
+  void* ws = fixed;
+  if (!ws) {
+    int rc = workspace(kWsSplit, bytes, s, &ws);
+    if (rc) return rc;
+  }
   p.splits = splits;
   p.split_keys = split_keys;
   p.o_part = (float*)ws;
@@ -232,6 +268,7 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_NOMEM: return "device workspace allocation failed";
     case ATTN_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
     case ATTN_ERR_SIZE: return "problem too large for 32-bit in-kernel indexing";
+    case ATTN_ERR_SCRATCH: return "split-KV partials exceed the fixed scratch of attn_fwd_splitkv_noalloc";
     default: return "unknown status code";
   }
 }
@@ -443,6 +480,29 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (rc) return rc;
   return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, splits, split_keys, dtype,
                      (hipStream_t)stream);
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                             int Hkv, int Sq, int Sk, int d, float scale, int causal, int num_splits, int pack_gqa,
+                             int dtype, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  int rc = check_common(B, Hq, Hkv, Sq, Sk, d, scale);
+  if (rc) return rc;
+  int pack = 0, splits = 0, split_keys = 0;
+  rc = pack_choice(pack_gqa, Hq, Hkv, Sq, &pack);
+  if (rc) return rc;
+  rc = split_plan(dense_tiles(B, Hq, Hkv, Sq, pack), Sk, d, num_splits, &splits, &split_keys);
+  if (rc) return rc;
+  void* fixed = nullptr;
+  if (splits > 1) {
+    size_t ob = 0;
+    if (split_partials_bytes(splits, (size_t)B * Sq * Hq, d, &ob) > kScratchBytes) return ATTN_ERR_SCRATCH;
+    rc = scratch_address(&fixed);
+    if (rc) return rc;
+  }
+  return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, splits, split_keys, dtype,
+                     (hipStream_t)stream, fixed);
 }
 
 int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,

@@ -78,7 +78,8 @@ enum attn_status {
   ATTN_ERR_ARG = -6,      /* scale not finite or not > 0; unsupported combo    */
   ATTN_ERR_NOMEM = -7,    /* workspace allocation failed                       */
   ATTN_ERR_HIP = -8,      /* a HIP runtime call or kernel launch failed        */
-  ATTN_ERR_SIZE = -9      /* a size or index would overflow 32-bit addressing  */
+  ATTN_ERR_SIZE = -9,     /* a size or index would overflow 32-bit addressing  */
+  ATTN_ERR_SCRATCH = -10  /* attn_fwd_splitkv_noalloc: partials exceed its scratch */
 };
 
 /*
@@ -207,6 +208,32 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                      int num_splits, int pack_gqa, int dtype, void* stream);
+
+/* Bytes of the fixed device scratch of attn_fwd_splitkv_noalloc (per GPU). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops (decoding), harnesses that forbid hipMalloc.  Same arguments, plan
+ * (attn_split_plan) and result as attn_fwd_splitkv; the caller still passes
+ * q, k, v, o and lse.  The split-KV partials go to a fixed device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES (16 MiB) compiled into the library, one per
+ * GPU, held until the process ends, instead of the lazily grown workspace:
+ * the call never allocates or frees memory.  The partials of a plan take
+ * splits * B * Sq * Hq * (d + 1) floats (two parts, each rounded up to 256
+ * bytes); a plan that needs more returns ATTN_ERR_SCRATCH and enqueues
+ * nothing (e.g. the decode shape B=4 Hq=32 Sq=1 d=128 with 8 ranges takes
+ * 129 KiB).  With one range no partials are written.  Every call on a GPU
+ * shares that GPU's array and leaves its partials there; each call writes
+ * every partial it reads, so nothing needs clearing, but calls that overlap
+ * on one GPU (different streams, threads) race on it and must be ordered by
+ * the caller.  The array's device address is looked up once per device on
+ * the first call there (hipGetSymbolAddress).
+ */
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                             int num_splits, int pack_gqa, int dtype, void* stream);
 
 /*
  * attn_split_plan -- the plan attn_fwd_splitkv follows for these arguments:

@@ -285,4 +285,17 @@ def test_every_status_code_is_covered():
     # test_validation_errors / test_other_entry_points_validate
     src = open(os.path.join(ROOT, "include", "attn.h")).read()
     codes = dict((n, int(v)) for n, v in re.findall(r"(ATTN_ERR_\w+)\s*=\s*(-\d+)", src))
-    assert set(codes.values()) == {-1, -2, -3, -4, -5, -6, -7, -8, -9}
+    assert set(codes.values()) == {-1, -2, -3, -4, -5, -6, -7, -8, -9, -10}
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch(lib):
+    # 16 MiB of partials: B=64 Sq=32 Hq=32 d=128 with 8 ranges needs
+    # 8 * 65536 * 129 floats = 258 MiB -> ATTN_ERR_SCRATCH before anything runs
+    rc = lib.attn_fwd_splitkv_noalloc(FAKE, FAKE, FAKE, FAKE, None, 64, 32, 8, 32, 16384, 128, 0.1, 0, 8, 0, 0,
+                                      None)
+    assert rc == -10
+    assert b"scratch" in lib.attn_strerror(rc)
+    assert lib.attn_fwd_splitkv_noalloc(None, FAKE, FAKE, FAKE, None, 1, 2, 2, 1, 256, 128, 0.1, 0, 0, -1, 0,
+                                        None) == -1
+    assert lib.attn_fwd_splitkv_noalloc(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 2, 1, 256, 128, 0.1, 0, 0, -1, 2,
+                                        None) == -5
