@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fwd_splitkv", "fwd_splitkv_noalloc", "combine", "split_plan", "library",
+__all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fp8_prepass_qkv", "fwd_splitkv", "fwd_splitkv_noalloc", "combine", "split_plan", "library",
            "default_signs", "tile_of",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
@@ -52,6 +52,8 @@ def library() -> ctypes.CDLL:
     L.attn_fwd.restype = I
     L.attn_fp8_prepass.argtypes = [P, P, P, I, I, I, I, I, P, P]
     L.attn_fp8_prepass.restype = I
+    L.attn_fp8_prepass_qkv.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+    L.attn_fp8_prepass_qkv.restype = I
     L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     L.attn_fwd_fp8.restype = I
     L.attn_default_signs.argtypes = [ctypes.POINTER(ctypes.c_float), I]
@@ -77,6 +79,8 @@ def library() -> ctypes.CDLL:
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_release.argtypes = []
     L.attn_release.restype = None
+    L.attn_clock_probe.argtypes = [P, I, IP, P]
+    L.attn_clock_probe.restype = I
     L.attn_test_fail_next.argtypes = [I]
     L.attn_test_fail_next.restype = I
     _lib = L
@@ -314,6 +318,27 @@ def fp8_prepass(x: torch.Tensor, transpose_out: bool = False,
                                     _ptr(signs), _stream())
     _check(rc, "attn_fp8_prepass")
     return x8, ds
+
+
+def fp8_prepass_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, signs: Optional[torch.Tensor] = None):
+    """Quantise Q, K and V in one launch (``attn_fp8_prepass_qkv``): fp32
+    q [B, Sq, Hq, 128], k/v [B, Sk, Hkv, 128] -> (q8, k8, v8t, q_descale,
+    k_descale, v_descale) in the layouts ``fwd_fp8`` takes (v8t is
+    [B, Hkv, 128, Sk]); signs (128 device floats) rotate Q and K."""
+    _need_gpu(q, k, v, signs)
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    dev = q.device
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    v8t = torch.empty((B, Hkv, d, Sk), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, Hq, (Sq + 127) // 128), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, Hkv, (Sk + 127) // 128), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    rc = library().attn_fp8_prepass_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(qs),
+                                        _ptr(ks), _ptr(vs), B, Hq, Hkv, Sq, Sk, d, _ptr(signs), _stream())
+    _check(rc, "attn_fp8_prepass_qkv")
+    return q8, k8, v8t, qs, ks, vs
 
 
 def fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, causal: bool = False,

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip",
-           "attn_bwd_dkdv.hip", "attn_bwd_dq.hip"]
+           "attn_bwd_dkdv.hip", "attn_bwd_dq.hip", "attn_clock.hip"]
 ARCH = "gfx950"
 
 

@@ -331,6 +331,24 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+namespace {
+attn::PrepassSeg prepass_seg(const float* x, uint8_t* x8, float* descale, int B, int S, int H, int transpose,
+                             const float* signs, int default_signs) {
+  attn::PrepassSeg g{};
+  g.x = x;
+  g.x8 = x8;
+  g.descale = descale;
+  g.signs = signs;
+  g.default_signs = default_signs;
+  g.B = B;
+  g.S = S;
+  g.H = H;
+  g.transpose = transpose ? 1 : 0;
+  g.blocks = B * H * ((S + 127) / 128);
+  return g;
+}
+}  // namespace
+
 int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, int H, int d,
                      int transpose_out, const float* signs, void* stream) {
   if (!x || !x8 || !descale) return ATTN_ERR_NULL;
@@ -338,16 +356,28 @@ int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, 
   if (d != 128) return ATTN_ERR_HEADDIM;
   if ((long long)B * S * H * d > kMax32 * 2) return ATTN_ERR_SIZE;
   attn::PrepassParams p{};
-  p.x = x;
-  p.x8 = x8;
-  p.descale = descale;
-  p.signs = signs;
-  p.default_signs = 0;
-  p.B = B;
-  p.S = S;
-  p.H = H;
+  p.seg[0] = prepass_seg(x, x8, descale, B, S, H, transpose_out, signs, 0);
+  p.nseg = 1;
   p.d = d;
-  p.transpose_out = transpose_out ? 1 : 0;
+  hipError_t e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_prepass(p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_fp8_prepass_qkv(const float* q, const float* k, const float* v, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                         float* q_descale, float* k_descale, float* v_descale, int B, int Hq, int Hkv, int Sq,
+                         int Sk, int d, const float* signs, void* stream) {
+  if (!q || !k || !v || !q8 || !k8 || !v8t || !q_descale || !k_descale || !v_descale) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if ((long long)B * Sq * Hq * d > kMax32 * 2 || (long long)B * Sk * Hkv * d > kMax32 * 2) return ATTN_ERR_SIZE;
+  if ((long long)B * Hq * ((Sq + 127) / 128) + 2LL * B * Hkv * ((Sk + 127) / 128) > kMax32) return ATTN_ERR_SIZE;
+  attn::PrepassParams p{};
+  p.seg[0] = prepass_seg(q, q8, q_descale, B, Sq, Hq, 0, signs, 0);
+  p.seg[1] = prepass_seg(k, k8, k_descale, B, Sk, Hkv, 0, signs, 0);
+  p.seg[2] = prepass_seg(v, v8t, v_descale, B, Sk, Hkv, 1, nullptr, 0);
+  p.nseg = 3;
+  p.d = d;
   hipError_t e = launch_gate();
   if (e == hipSuccess) e = attn::launch_prepass(p, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
@@ -386,28 +416,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     float* qs = (float*)(v8t + al(kb));
     float* ks = (float*)((uint8_t*)qs + sq_b);
     float* vs = (float*)((uint8_t*)ks + sk_b);
-    // the Hadamard type rotates Q and K with the default signs, which the
-    // prepass kernel holds in constant memory
-    auto prepass = [&](const float* x, uint8_t* x8, float* ds, int S, int H, int transpose, int rotate) {
-      attn::PrepassParams pp{};
-      pp.x = x;
-      pp.x8 = x8;
-      pp.descale = ds;
-      pp.signs = nullptr;
-      pp.default_signs = rotate;
-      pp.B = B;
-      pp.S = S;
-      pp.H = H;
-      pp.d = d;
-      pp.transpose_out = transpose;
-      hipError_t e = launch_gate();
-      if (e == hipSuccess) e = attn::launch_prepass(pp, s);
-      return e == hipSuccess ? ATTN_OK : hip_fail(e);
-    };
+    // one launch quantises Q, K and V^T; the Hadamard type rotates Q and K
+    // with the default signs, which the prepass kernel holds in constant memory
     const int rot = dtype == ATTN_FP8_E4M3_HADAMARD ? 1 : 0;
-    rc = prepass((const float*)q, q8, qs, Sq, Hq, 0, rot);
-    if (!rc) rc = prepass((const float*)k, k8, ks, Sk, Hkv, 0, rot);
-    if (!rc) rc = prepass((const float*)v, v8t, vs, Sk, Hkv, 1, 0);
+    attn::PrepassParams pp{};
+    pp.seg[0] = prepass_seg((const float*)q, q8, qs, B, Sq, Hq, 0, nullptr, rot);
+    pp.seg[1] = prepass_seg((const float*)k, k8, ks, B, Sk, Hkv, 0, nullptr, rot);
+    pp.seg[2] = prepass_seg((const float*)v, v8t, vs, B, Sk, Hkv, 1, nullptr, 0);
+    pp.nseg = 3;
+    pp.d = d;
+    hipError_t e = launch_gate();
+    if (e == hipSuccess) e = attn::launch_prepass(pp, s);
+    rc = e == hipSuccess ? ATTN_OK : hip_fail(e);
     if (!rc) rc = attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream);
     return rc;
   }
@@ -585,6 +605,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.grid_dkdv = (int)(Hkv * nkb);
   hipError_t e = launch_gate();
   if (e == hipSuccess) e = attn::launch_bwd(p, dtype, d, causal, varlen ? 1 : 0, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_clock_probe(unsigned long long* out, int wall_ticks, int* wall_khz, void* stream) {
+  if (!out || !wall_khz) return ATTN_ERR_NULL;
+  if (wall_ticks <= 0) return ATTN_ERR_ARG;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e == hipSuccess) e = launch_gate();
+  if (e == hipSuccess) e = attn::launch_clock_probe(out, wall_ticks, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -29,9 +29,17 @@ int fwd_fp8_block_m() { return 128; }
 // prepass
 // ============================================================================
 //
-// One workgroup of 256 threads per block of 128 rows; thread t owns row t/2,
-// channels 64*(t%2) .. +63, in registers.  The rotation's last butterfly
-// stage (distance 64) pairs the two threads of a row, neighbouring lanes.
+// One workgroup of 256 threads per block of 128 rows of one (batch, head) of
+// one tensor; a launch covers up to three tensors (segments), so the Q, K and
+// V^T of the fp8 forward are quantised in one launch.  Three block paths:
+//  * row-major codes, no rotation: coalesced loads (in each load, lanes 0-31
+//    read one 512-byte row and lanes 32-63 another), 128-byte code rows out;
+//  * transposed codes (V^T), no rotation: the same coalesced loads, each lane
+//    keeping 16 consecutive rows of its 4 channels, a byte transpose in
+//    registers (v_perm) and in LDS, and 128-byte code rows of V^T out;
+//  * rotation: thread t owns row t/2, channels 64 (t % 2) .. +63, in
+//    registers; the rotation's last butterfly stage (distance 64) pairs the
+//    two threads of a row, neighbouring lanes.
 
 __device__ __forceinline__ float lane_xor1(float x) {
   // value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2])
@@ -51,36 +59,76 @@ constexpr SignTable make_default_signs() {
 }
 __constant__ SignTable kDefaultSigns = make_default_signs();
 
-__global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
+// Streaming accesses: every input element is read once and every code
+// written once, so the coalesced paths load and all paths store through the
+// non-temporal path (no cache allocation; measured 8-12% faster on the
+// c3fp8 / c5 tensors, where the one-launch prepass then moves its bytes as
+// fast as a plain device copy).
+typedef float nf4 __attribute__((ext_vector_type(4)));
+typedef unsigned nu4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const nf4 t = __builtin_nontemporal_load((const nf4*)p);
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void store_stream(uint8_t* p, nu4 v) { __builtin_nontemporal_store(v, (nu4*)p); }
+
+// correctly rounded v / s (Markstein: q0 within one ulp of the quotient, the
+// remainder v - q0 s exact in one FMA, one more FMA q0 + r inv rounds to the
+// nearest quotient; a subnormal quotient may be one ulp off, which no E4M3
+// code resolves: they all map to zero), then clipped to the E4M3 range
+__device__ __forceinline__ float quot_clip(float v, float s, float inv) {
+  const float q0 = v * inv;
+  const float r = __builtin_fmaf(-q0, s, v);
+  return fminf(fmaxf(__builtin_fmaf(r, inv, q0), -448.0f), 448.0f);
+}
+
+// block amax of the workgroup: per-lane value -> every thread
+__device__ __forceinline__ float block_amax(float am, float* red, int tid) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(256) prepass_kernel(PrepassParams pp) {
   constexpr int ROWS = 128, D = 128, HALF = 64;
-  const int nblk = (p.S + ROWS - 1) / ROWS;
-  const int blk = blockIdx.x % nblk;
-  const int h = (blockIdx.x / nblk) % p.H;
-  const int b = blockIdx.x / (nblk * p.H);
+  // this workgroup's segment and block
+  int si = 0, local = blockIdx.x;
+  while (si + 1 < pp.nseg && local >= pp.seg[si].blocks) {
+    local -= pp.seg[si].blocks;
+    ++si;
+  }
+  const PrepassSeg g = pp.seg[si];
+  const int nblk = (g.S + ROWS - 1) / ROWS;
+  const int blk = local % nblk;
+  const int h = (local / nblk) % g.H;
+  const int b = local / (nblk * g.H);
   const int tid = threadIdx.x;
-  const int r = tid >> 1, half = tid & 1;
   const int row0 = blk * ROWS;
-  const int nrows = min(ROWS, p.S - row0);
-  const bool live = r < nrows;
+  const int nrows = min(ROWS, g.S - row0);
+  const int lane = tid & 63, w = tid >> 6;
 
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tT[D][ROWS + 16];   // transposed codes
+  // transposed codes; a 176-byte row stride spreads the 16-byte writes of
+  // neighbouring channels over the banks
+  __shared__ __attribute__((aligned(16))) uint8_t tT[D][ROWS + 48];
 
-  const float* signs = p.default_signs ? kDefaultSigns.v : p.signs;
-  if (signs == nullptr && !p.transpose_out) {
-    // Row-major codes without rotation: no thread needs a whole row, so the
-    // lanes read coalesced -- in each load, lanes 0-31 read one 512-byte row
-    // and lanes 32-63 the next -- and write 128-byte rows of codes.  Wave w
-    // covers rows 32 w .. 32 w + 31, two per load.
-    const int lane = tid & 63, w = tid >> 6;
-    const int c4 = 4 * (lane & 31);       // first of the lane's 4 channels
+  const float* signs = g.default_signs ? kDefaultSigns.v : g.signs;
+  if (signs == nullptr) {
+    // coalesced: lane half hl of wave w reads rows 32 w + 16 hl + k (k-th
+    // load) for transposed output, 32 w + 2 k + hl for row-major output, 4
+    // channels c4 .. c4 + 3 each
+    const int hl = lane >> 5;
+    const int c4 = 4 * (lane & 31);
+    auto row_of = [&](int k) { return g.transpose ? 32 * w + 16 * hl + k : 32 * w + 2 * k + hl; };
     float4 xv[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int rr = 32 * w + 2 * k + (lane >> 5);
+      const int rr = row_of(k);
       if (rr < nrows) {
-        const long long ri = ((long long)b * p.S + row0 + rr) * p.H + h;
-        xv[k] = *(const float4*)(p.x + ri * D + c4);
+        const long long ri = ((long long)b * g.S + row0 + rr) * g.H + h;
+        xv[k] = load_stream(g.x + ri * D + c4);
       } else {
         xv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -89,54 +137,71 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       am = fmaxf(fmaxf(am, fmaxf(fabsf(xv[k].x), fabsf(xv[k].y))), fmaxf(fabsf(xv[k].z), fabsf(xv[k].w)));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-    if (lane == 0) red[w] = am;
-    __syncthreads();
-    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    am = block_amax(am, red, tid);
     const float s = am > 0.f ? am / 448.0f : 1.0f;
-    if (tid == 0) p.descale[((long long)b * p.H + h) * nblk + blk] = s;
+    if (tid == 0) g.descale[((long long)b * g.H + h) * nblk + blk] = s;
     const float inv = 1.0f / s;
-    auto quant = [&](float v) {
-      // correctly rounded v / s (Markstein: q0 within one ulp, exact
-      // remainder, one correcting FMA), clipped
-      const float q0 = v * inv;
-      const float r = __builtin_fmaf(-q0, s, v);
-      return fminf(fmaxf(__builtin_fmaf(r, inv, q0), -448.0f), 448.0f);
-    };
+    uint32_t code[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int rr = 32 * w + 2 * k + (lane >> 5);
-      int code = __builtin_amdgcn_cvt_pk_fp8_f32(quant(xv[k].x), quant(xv[k].y), 0, false);
-      code = __builtin_amdgcn_cvt_pk_fp8_f32(quant(xv[k].z), quant(xv[k].w), code, true);
-      if (rr < nrows) {
-        const long long ri = ((long long)b * p.S + row0 + rr) * p.H + h;
-        *(int*)(p.x8 + ri * D + c4) = code;
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot_clip(xv[k].x, s, inv), quot_clip(xv[k].y, s, inv), 0, false);
+      code[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot_clip(xv[k].z, s, inv), quot_clip(xv[k].w, s, inv),
+                                                         c, true);
+    }
+    if (!g.transpose) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int rr = row_of(k);
+        if (rr < nrows) {
+          const long long ri = ((long long)b * g.S + row0 + rr) * g.H + h;
+          __builtin_nontemporal_store(code[k], (uint32_t*)(g.x8 + ri * D + c4));
+        }
       }
+      return;
     }
-    return;
-  }
-
-  // ---- load the thread's 64 channels of its row
-  float x[HALF];
-  const long long rowidx = ((long long)b * p.S + row0 + r) * p.H + h;
-  const float* src = p.x + rowidx * D + half * HALF;
-  if (live) {
+    // byte transpose of 4 rows x 4 channels at a time: col[j] holds channel
+    // c4 + j of rows 4 i .. 4 i + 3 (v_perm picks bytes of {S0, S1}, S1 low)
+    uint32_t col[4][4];
 #pragma unroll
-    for (int i = 0; i < HALF; i += 4) {
-      const float4 v = *(const float4*)(src + i);
-      x[i] = v.x;
-      x[i + 1] = v.y;
-      x[i + 2] = v.z;
-      x[i + 3] = v.w;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c0 = code[4 * i], c1 = code[4 * i + 1], c2 = code[4 * i + 2], c3 = code[4 * i + 3];
+      const uint32_t lo01 = __builtin_amdgcn_perm(c1, c0, 0x05010400u);   // c0.0 c1.0 c0.1 c1.1
+      const uint32_t hi01 = __builtin_amdgcn_perm(c1, c0, 0x07030602u);   // c0.2 c1.2 c0.3 c1.3
+      const uint32_t lo23 = __builtin_amdgcn_perm(c3, c2, 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(c3, c2, 0x07030602u);
+      col[0][i] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      col[1][i] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+      col[2][i] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+      col[3][i] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(uint4*)(&tT[c4 + j][32 * w + 16 * hl]) = make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
   } else {
+    // ---- rotation: the thread's 64 channels of row r
+    const int r = tid >> 1, half = tid & 1;
+    const bool live = r < nrows;
+    float x[HALF];
+    const long long rowidx = ((long long)b * g.S + row0 + r) * g.H + h;
+    const float* src = g.x + rowidx * D + half * HALF;
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) x[i] = 0.f;
-  }
-
-  // ---- optional rotation: x <- (x * signs) H_128 / sqrt(128), in fp32
-  if (signs != nullptr) {
+      for (int i = 0; i < HALF; i += 4) {
+        // cached loads: a lane reads 256 contiguous bytes across these 16
+        // loads while a load instruction touches 64 separate 16-byte pieces,
+        // so each cache line serves several instructions (streaming loads,
+        // which do not allocate, fetched the lines again: twice as slow)
+        const float4 v = *(const float4*)(src + i);
+        x[i] = v.x;
+        x[i + 1] = v.y;
+        x[i + 2] = v.z;
+        x[i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) x[i] = 0.f;
+    }
+    // x <- (x * signs) H_128 / sqrt(128), in fp32
 #pragma unroll
     for (int i = 0; i < HALF; ++i) x[i] *= signs[half * HALF + i];
 #pragma unroll
@@ -157,71 +222,54 @@ __global__ void __launch_bounds__(256) prepass_kernel(PrepassParams p) {
     const float norm = 0.08838834764831845f;   // 1 / sqrt(128)
 #pragma unroll
     for (int i = 0; i < HALF; ++i) x[i] *= norm;
-  }
-
-  // ---- block amax
-  float am = 0.f;
+    float am = 0.f;
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) am = fmaxf(am, fabsf(x[i]));
+    for (int i = 0; i < HALF; ++i) am = fmaxf(am, fabsf(x[i]));
+    am = block_amax(am, red, tid);
+    const float s = am > 0.f ? am / 448.0f : 1.0f;
+    if (tid == 0) g.descale[((long long)b * g.H + h) * nblk + blk] = s;
+    const float inv = 1.0f / s;
+    uint32_t q[HALF / 4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  if ((tid & 63) == 0) red[tid >> 6] = am;
-  __syncthreads();
-  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = am > 0.f ? am / 448.0f : 1.0f;
-  if (tid == 0) p.descale[((long long)b * p.H + h) * nblk + blk] = s;
-
-  // ---- quantise: E4M3(clip(x / s)), round to nearest even.  x / s is the
-  // correctly rounded fp32 quotient, formed from the correctly rounded
-  // reciprocal: q0 = x * inv is within one ulp of x / s, the remainder
-  // x - q0 s is exact in one FMA, and one more FMA q0 + r inv rounds to the
-  // nearest quotient (Markstein's division theorem; a subnormal quotient may
-  // be one ulp off, which no E4M3 code resolves: they all map to zero)
-  const float inv = 1.0f / s;
-  auto divide = [&](float v) {
-    const float q0 = v * inv;
-    const float r = __builtin_fmaf(-q0, s, v);
-    return __builtin_fmaf(r, inv, q0);
-  };
-  uint32_t q[HALF / 4];
-#pragma unroll
-  for (int i = 0; i < HALF; i += 4) {
-    float y[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(divide(x[i + j]), -448.0f), 448.0f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-    q[i / 4] = (uint32_t)w;
-  }
-
-  if (!p.transpose_out) {
-    if (live) {
-      uint8_t* dst = p.x8 + rowidx * D + half * HALF;
-#pragma unroll
-      for (int i = 0; i < HALF / 16; ++i)
-        *(uint4*)(dst + 16 * i) = make_uint4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+    for (int i = 0; i < HALF; i += 4) {
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot_clip(x[i], s, inv), quot_clip(x[i + 1], s, inv), 0, false);
+      q[i / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot_clip(x[i + 2], s, inv), quot_clip(x[i + 3], s, inv),
+                                                          c, true);
     }
-    return;
+    if (!g.transpose) {
+      if (live) {
+        uint8_t* dst = g.x8 + rowidx * D + half * HALF;
+#pragma unroll
+        for (int i = 0; i < HALF / 16; ++i)
+          store_stream(dst + 16 * i, nu4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]});
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) tT[half * HALF + i][r] = (uint8_t)(q[i >> 2] >> (8 * (i & 3)));
   }
 
-  // ---- transposed output [B, H, d, S] through LDS
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) tT[half * HALF + i][r] = (uint8_t)(q[i >> 2] >> (8 * (i & 3)));
+  // ---- transposed output [B, H, d, S]: 8 consecutive lanes write one
+  // channel's 128 bytes of the block
   __syncthreads();
-  const int c = tid >> 1;                 // channel written by this thread
-  const int s0 = (tid & 1) * HALF;        // its 64 tokens of the block
-  uint8_t* dst = p.x8 + (((long long)b * p.H + h) * D + c) * p.S + row0 + s0;
-  if (s0 + HALF <= nrows && ((p.S & 15) == 0)) {
+  const long long plane = ((long long)b * g.H + h) * D;
+  if (nrows == ROWS && (g.S & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < HALF / 16; ++i) *(uint4*)(dst + 16 * i) = *(const uint4*)(&tT[c][s0 + 16 * i]);
+    for (int i = 0; i < 4; ++i) {
+      const int c = 32 * i + (tid >> 3), piece = tid & 7;
+      store_stream(g.x8 + (plane + c) * g.S + row0 + 16 * piece, *(const nu4*)(&tT[c][16 * piece]));
+    }
   } else {
-    for (int i = 0; i < HALF && s0 + i < nrows; ++i) dst[i] = tT[c][s0 + i];
+    for (int i = tid; i < D * nrows; i += 256) {
+      const int c = i / nrows, t = i % nrows;
+      g.x8[(plane + c) * g.S + row0 + t] = tT[c][t];
+    }
   }
 }
 
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
-  const int nblk = (p.S + 127) / 128;
-  const long long grid = (long long)p.B * p.H * nblk;
+  long long grid = 0;
+  for (int i = 0; i < p.nseg; ++i) grid += p.seg[i].blocks;
   hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -94,14 +94,24 @@ struct Fp8FwdParams {
   int grid;
 };
 
-struct PrepassParams {
-  const float* x;             // [B, S, H, d]
-  uint8_t* x8;                // [B, S, H, d] or [B, H, d, S]
-  float* descale;             // [B, H, ceil(S/128)]
-  const float* signs;         // d signs (device) or nullptr
+// One tensor of the fp8 prepass: x [B, S, H, d] fp32 -> codes x8 ([B, S, H, d],
+// or [B, H, d, S] when transpose) and scales descale [B, H, ceil(S/128)].
+struct PrepassSeg {
+  const float* x;
+  uint8_t* x8;
+  float* descale;
+  const float* signs;         // d signs (device) for the rotation, or nullptr
   int default_signs;          // non-zero: rotate with the built-in default signs (signs ignored)
-  int B, S, H, d;
-  int transpose_out;
+  int B, S, H;
+  int transpose;
+  int blocks;                 // B * H * ceil(S / 128): workgroups of this tensor
+};
+// Up to three tensors in one launch (Q, K and V^T for the fp8 forward):
+// workgroup i belongs to segment s when first[s] <= i < first[s] + seg[s].blocks.
+struct PrepassParams {
+  PrepassSeg seg[3];
+  int nseg;
+  int d;
 };
 
 // splitmix64 (Steele, Lea, Flood 2014): the output for counter value x
@@ -144,5 +154,7 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, int causal, int v
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
 constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 hipError_t launch_prepass(const PrepassParams& p, hipStream_t s);
+// shader-clock and wall-clock deltas of one lane over `ticks` wall-clock ticks
+hipError_t launch_clock_probe(unsigned long long* out, long long ticks, hipStream_t s);
 
 }  // namespace attn

@@ -136,6 +136,23 @@ int attn_fp8_prepass(const float* x, uint8_t* x8, float* descale, int B, int S, 
                      int transpose_out, const float* signs, void* stream);
 
 /*
+ * attn_fp8_prepass_qkv -- attn_fp8_prepass of Q, K and V in one launch, in
+ * the layouts attn_fwd_fp8 takes: q [B, Sq, Hq, d] -> q8 [B, Sq, Hq, d] and
+ * q_descale [B, Hq, ceil(Sq/128)]; k [B, Sk, Hkv, d] -> k8 [B, Sk, Hkv, d]
+ * and k_descale [B, Hkv, ceil(Sk/128)]; v [B, Sk, Hkv, d] -> v8t
+ * [B, Hkv, d, Sk] (token index innermost) and v_descale [B, Hkv,
+ * ceil(Sk/128)].  signs (d device floats, or NULL) rotate Q and K as in
+ * attn_fp8_prepass; V is never rotated ("FlashAttention-3 Deep Dive",
+ * section 4: the rotation of Q and K leaves Q K^T unchanged).  The codes and
+ * scales are those the three single calls write.  All pointers device and
+ * caller-owned; d must be 128.  Returns ATTN_OK, ATTN_ERR_NULL,
+ * ATTN_ERR_SHAPE, ATTN_ERR_HEADDIM, ATTN_ERR_SIZE or ATTN_ERR_HIP.
+ */
+int attn_fp8_prepass_qkv(const float* q, const float* k, const float* v, uint8_t* q8, uint8_t* k8,
+                         uint8_t* v8t, float* q_descale, float* k_descale, float* v_descale, int B,
+                         int Hq, int Hkv, int Sq, int Sk, int d, const float* signs, void* stream);
+
+/*
  * attn_fwd_fp8 -- fused attention forward on pre-quantised E4M3 operands,
  * fp32 accumulation in both GEMMs, bf16 output.
  *   q8 [B, Sq, Hq, d] codes, k8 [B, Sk, Hkv, d] codes,
@@ -329,6 +346,16 @@ const char* attn_strerror(int code);
  * statistics) on every device that has them.  Waits for each such device to
  * finish its queued work first (hipDeviceSynchronize). */
 void attn_release(void);
+
+/* Measurement aid: the shader clock of one compute unit while other work
+ * runs.  Enqueues one wave that spins for wall_ticks ticks of the device's
+ * constant-rate wall clock (hipDeviceAttributeWallClockRate, written to
+ * *wall_khz on the host) and writes to out (2 device uint64) the shader-clock
+ * and wall-clock deltas it saw: clock = out[0] / out[1] * wall_khz kHz.
+ * Run it on a second stream beside the kernel being measured (the wave
+ * takes one SIMD of one compute unit while it spins).  Returns ATTN_OK,
+ * ATTN_ERR_NULL, ATTN_ERR_ARG or ATTN_ERR_HIP. */
+int attn_clock_probe(unsigned long long* out, int wall_ticks, int* wall_khz, void* stream);
 
 /* Failure injection for tests of the error paths (the failures a host-only
  * test cannot otherwise produce).  Arms a one-shot failure for the calling

@@ -71,6 +71,30 @@ def test_other_entry_points_validate(lib):
     assert lib.attn_strerror(12345) == b"unknown status code"
 
 
+def test_prepass_qkv_validates(lib):
+    ok = [FAKE] * 9 + [1, 2, 2, 128, 128, 128, None, None]
+    for i in range(9):
+        a = list(ok)
+        a[i] = None
+        assert lib.attn_fp8_prepass_qkv(*a) == -1
+    for i, bad in ((9, 0), (10, 0), (11, -1), (12, 0), (13, 0)):
+        a = list(ok)
+        a[i] = bad
+        assert lib.attn_fp8_prepass_qkv(*a) == -2
+    a = list(ok)
+    a[14] = 64
+    assert lib.attn_fp8_prepass_qkv(*a) == -3
+    assert lib.attn_test_fail_next(-8) == 0
+    assert lib.attn_fp8_prepass_qkv(*ok) == -8
+
+
+def test_clock_probe_validates(lib):
+    k = ctypes.c_int()
+    assert lib.attn_clock_probe(None, 100, ctypes.byref(k), None) == -1
+    assert lib.attn_clock_probe(FAKE, 100, None, None) == -1
+    assert lib.attn_clock_probe(FAKE, 0, ctypes.byref(k), None) == -6
+
+
 def test_default_signs_match_generator(lib):
     assert ea.default_signs(128) == W.hadamard_signs(128, 55).tolist()
 

@@ -116,6 +116,31 @@ def test_prepass_rotation_within_one_code(ea):
     np.testing.assert_allclose(sc.cpu().numpy(), rs, rtol=2.0 ** -22)
 
 
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("shape", [(1, 256, 256, 4, 2), (2, 300, 200, 2, 1), (1, 17, 1040, 3, 3)])
+def test_prepass_qkv_one_launch(ea, rotate, shape):
+    # the one-launch prepass of Q, K and V^T writes what the three single
+    # calls write, and (without rotation) what the oracle quantiser writes
+    B, Sq, Sk, Hq, Hkv = shape
+    print(f"[case] prepass qkv rotate={rotate} shape={shape}", flush=True)
+    q, _, _ = W.make_dense(B, Sq, Sq, Hq, Hkv, 128, "fp8", seed=23, outliers=True)
+    _, k, v = W.make_dense(B, Sk, Sk, Hq, Hkv, 128, "fp8", seed=24, outliers=True)
+    signs = torch.from_numpy(W.hadamard_signs()).cuda() if rotate else None
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    got = ea.fp8_prepass_qkv(qc, kc, vc, signs=signs)
+    q8, qs = ea.fp8_prepass(qc, signs=signs)
+    k8, ks = ea.fp8_prepass(kc, signs=signs)
+    v8t, vs = ea.fp8_prepass(vc, transpose_out=True)
+    torch.cuda.synchronize()
+    for a, b in zip(got, (q8, k8, v8t, qs, ks, vs)):
+        assert torch.equal(a, b)
+    if not rotate:
+        for x, c8, sc, tr in ((q, got[0], got[3], False), (k, got[1], got[4], False), (v, got[2], got[5], True)):
+            rc, rs = F.block_quantize(x.numpy())
+            np.testing.assert_array_equal(c8.cpu().numpy(), np.transpose(rc, (0, 2, 3, 1)) if tr else rc)
+            np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+
+
 def oracle_fp8(q, k, v, causal, scale, signs=None):
     """Oracle on the dequantised inputs: quantise (after the optional rotation
     of Q and K, rounded to fp32) with the oracle quantiser, dequantise in

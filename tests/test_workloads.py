@@ -44,3 +44,17 @@ def test_c5_outliers_scaled():
     big = q[..., ch].abs().mean()
     small = q.abs().mean()
     assert big > 10 * small
+
+
+def test_flop_counts_match_the_oracle_rule():
+    # the bench's counting rule (workloads) equals the oracle's on every
+    # workload, so the throughput figures and the oracle agree on the work
+    from oracle.attention import attention_backward_flops, attention_flops
+    for name, w in W.CONFIGS.items():
+        if w.varlen:
+            lengths = W.varlen_lengths(total=w.Sq)
+            assert W.forward_flops(w) == attention_flops(0, 0, w.d, w.causal, H=w.Hq, lengths=lengths)
+        else:
+            assert W.forward_flops(w) == attention_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
+            assert W.backward_flops(w) == attention_backward_flops(w.Sq, w.Sk, w.d, w.causal, B=w.B, H=w.Hq)
+    assert W.forward_flops(W.CONFIGS["c3"]) == 1099645845504.0

@@ -175,3 +175,34 @@ def make_varlen(lengths, Hq, Hkv, d, dtype="fp16", seed=4321):
     v = _randn((T, Hkv, d), seed + 2)
     dt = TORCH_DTYPES[dtype]
     return q.to(dt), k.to(dt), v.to(dt), cu_seqlens_from_lengths(list(lengths))
+
+
+# ---------------------------------------------------------------- work counts
+# (bookkeeping for throughput figures: how many (query, key) pairs a
+# workload's mask leaves; no attention arithmetic)
+def unmasked_pairs(Sq: int, Sk: int, causal: bool) -> int:
+    """(query, key) pairs a row-major mask leaves: all of them, or with the
+    causal mask (key j hidden from query i when j > i) the lower triangle."""
+    if not causal:
+        return Sq * Sk
+    n = min(Sq, Sk)
+    return n * (n + 1) // 2 + max(0, Sq - Sk) * Sk
+
+
+def forward_flops(w: Workload, lengths: Optional[List[int]] = None) -> float:
+    """Algorithmic FLOP of one forward over workload w: 4 d per unmasked pair
+    (two GEMMs, a multiply and an add each)."""
+    if w.varlen:
+        lengths = varlen_lengths(total=w.Sq) if lengths is None else lengths
+        return 4.0 * w.d * w.Hq * sum(unmasked_pairs(n, n, w.causal) for n in lengths)
+    return 4.0 * w.d * w.B * w.Hq * unmasked_pairs(w.Sq, w.Sk, w.causal)
+
+
+def backward_flops(w: Workload, lengths: Optional[List[int]] = None) -> float:
+    """Algorithmic FLOP of one backward: five GEMMs of 2 d per unmasked pair."""
+    return 2.5 * forward_flops(w, lengths)
+
+
+def dense_convention_flops(w: Workload) -> Optional[float]:
+    """The 4 B H N^2 D count that also counts masked pairs (dense only)."""
+    return None if w.varlen else 4.0 * w.B * w.Hq * w.Sq * w.Sk * w.d
