@@ -696,7 +696,8 @@ static bool use_wide() {
   return wide;
 }
 
-// Softcap and / or column-major V: dense 4-wave (128-row) blocks
+// Softcap (with or without column-major V), and column-major V at d = 64:
+// dense 4-wave (128-row) blocks
 template <typename T, int D, int FEAT>
 static hipError_t launch_feat_t(const FwdParams& p, int causal, hipStream_t s) {
   return causal ? launch_one<T, D, 64, 4, true, false, false, false, FEAT>(p, s)
@@ -712,6 +713,13 @@ static hipError_t launch_feat_d(const FwdParams& p, int causal, hipStream_t s) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int causal, int varlen, hipStream_t s) {
+  if (p.feat == kFeatVCol && d == 128 && !varlen && use_wide()) {
+    // column-major V alone: the one-wave-per-SIMD kernel, on its 256-row tiles
+    FwdParams q = p;
+    q.tm = make_tile_map(p.B, p.Hq, p.Hkv, p.Sq, 256, causal);
+    q.grid = q.tm.ntiles;
+    return launch_fwd_wide(q, dtype, causal, s);
+  }
   if (p.feat != 0) {
     if (dtype == 0) return d == 128 ? launch_feat_d<__bf16, 128>(p, causal, s) : launch_feat_d<__bf16, 64>(p, causal, s);
     return d == 128 ? launch_feat_d<_Float16, 128>(p, causal, s) : launch_feat_d<_Float16, 64>(p, causal, s);

@@ -54,7 +54,12 @@ using ic = std::integral_constant<int, N>;
 // p.tm runs over (batch, head quadruple, 64-row block).  All four waves then
 // see the same keys, so a causal workgroup has no waves idling past their
 // diagonal while the last one finishes.
-template <typename T, bool CAUSAL, bool H4>
+// VCOL: V given column-major, [B, Hkv, D, Sk] (key index innermost; the
+// V_colmajor input of the FP8 layout discussion, "FlashAttention-3 Deep
+// Dive"): the V tile is D channel rows of 64 keys, and the second GEMM's
+// operand is read with one plain 16-byte read per fragment instead of two
+// transposing reads.
+template <typename T, bool CAUSAL, bool H4, bool VCOL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_wide_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -147,8 +152,18 @@ fwd_wide_kernel(FwdParams p) {
     const int pos = (wave * LOADS + i) * 64 + lane;
     const int row = pos / CPR, phys = pos % CPR;
     kdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_k<D>(row)) << 4));
-    vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+    if constexpr (VCOL) {
+      // V^T tile: D channel rows of BN keys = 8 chunks of 16 bytes, chunk c
+      // of row r stored at c ^ (r & 7); global rows are Sk keys apart
+      const int vr = pos / 8, vc = pos % 8;
+      vdma[i] = (uint32_t)(vr * p.Sk * 2 + ((vc ^ (vr & 7)) << 4));
+    } else {
+      vdma[i] = (uint32_t)(row * ks * 2 + ((phys ^ swz_v<D>(row)) << 4));
+    }
   }
+  static_assert(!VCOL || BN * 2 == 8 * 16, "V^T tile rows of 8 chunks");
+  // column-major V: this (batch, KV head)'s [D, Sk] plane
+  const T* Vt = VCOL ? (const T*)p.v + ((long long)b * p.Hkv + hkv) * D * p.Sk : nullptr;
   // the copies of tile t of K or V into ring buffer buf: source, size and
   // destination, all wave-uniform
   struct Copy {
@@ -156,14 +171,19 @@ fwd_wide_kernel(FwdParams p) {
     uint32_t bytes;
     char* dst;
   };
-  auto copy_of = [&](const T* base, int t, char* buf) {
+  auto copy_of = [&](const T* base, int t, char* buf, bool is_v) {
     const bool live = t < ntile;
     const int j0 = live ? t * BN : 0;
+    if (VCOL && is_v) {
+      // range to the end of the plane: keys past Sk read the next channel's
+      // (finite) values, or zeros past the plane; their P is 0
+      return Copy{(const void*)(Vt + j0), live ? (uint32_t)(D * p.Sk - j0) * 2u : 0u, buf + wave * LOADS * 1024};
+    }
     return Copy{(const void*)(base + (long long)j0 * ks),
                 live ? (uint32_t)(kv_len - j0) * (uint32_t)ks * 2u : 0u, buf + wave * LOADS * 1024};
   };
-  auto issue = [&](const T* src, int t, char* buf, const uint32_t(&off)[LOADS]) {
-    const Copy cp = copy_of(src, t, buf);
+  auto issue = [&](const T* src, int t, char* buf, const uint32_t(&off)[LOADS], bool is_v) {
+    const Copy cp = copy_of(src, t, buf, is_v);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) copy_row_to_lds(cp.src, cp.bytes, cp.dst + i * 1024, off[i]);
   };
@@ -188,7 +208,14 @@ fwd_wide_kernel(FwdParams p) {
   // (16 rows) and the second read (4 rows) are immediates, the ring slot is
   // added per iteration
   uint32_t vaddr[DB];
-  {
+  if constexpr (VCOL) {
+    // column-major: lane reads channel row 32 db + l32 (db: an immediate),
+    // keys 16 CC + 8 h .. + 7 = chunk 2 CC + h of the row, stored at
+    // (2 CC + h) ^ (l32 & 7)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      vaddr[cc] = lds0 + STAGES * TILE + l32 * 128 + ((((2 * cc + h) ^ (l32 & 7))) << 4);
+  } else {
     const int G = lane >> 4, i16 = lane & 15;
     const int r = 8 * h + (i16 >> 2);
     const int dd = 16 * (G & 1) + 4 * (i16 & 3);
@@ -196,6 +223,7 @@ fwd_wide_kernel(FwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) vaddr[db] = lds0 + STAGES * TILE + (voff0 ^ (uint32_t)(db << 6));
   }
+  static_assert(NC == DB, "one V address per chunk (column-major) or per channel block");
   // K fragments of k-step KK of the tile at byte offset kst into register
   // ring slot KK % 3
   auto read_k = [&](uint32_t kst, auto kk_tag) {
@@ -207,12 +235,21 @@ fwd_wide_kernel(FwdParams p) {
   // V chunk CC of the tile at byte offset vst into fragment buffer CC & 1
   auto read_v = [&](uint32_t vst, auto cc_tag) {
     constexpr int CC = decltype(cc_tag)::value;
-    constexpr int OFF = CC * 16 * ROW;
-    v_read<CC & 1, 0, OFF, 4 * ROW>(vaddr[0] + vst);
-    v_read<CC & 1, 1, OFF, 4 * ROW>(vaddr[1] + vst);
-    v_read<CC & 1, 2, OFF, 4 * ROW>(vaddr[2] + vst);
-    v_read<CC & 1, 3, OFF, 4 * ROW>(vaddr[3] + vst);
+    if constexpr (VCOL) {
+      vcol_read<CC & 1, 0, 0 * 32 * 128>(vaddr[CC] + vst);
+      vcol_read<CC & 1, 1, 1 * 32 * 128>(vaddr[CC] + vst);
+      vcol_read<CC & 1, 2, 2 * 32 * 128>(vaddr[CC] + vst);
+      vcol_read<CC & 1, 3, 3 * 32 * 128>(vaddr[CC] + vst);
+    } else {
+      constexpr int OFF = CC * 16 * ROW;
+      v_read<CC & 1, 0, OFF, 4 * ROW>(vaddr[0] + vst);
+      v_read<CC & 1, 1, OFF, 4 * ROW>(vaddr[1] + vst);
+      v_read<CC & 1, 2, OFF, 4 * ROW>(vaddr[2] + vst);
+      v_read<CC & 1, 3, OFF, 4 * ROW>(vaddr[3] + vst);
+    }
   };
+  // LDS operations one V chunk's reads add to the counter
+  constexpr int VREADS = VCOL ? DB : 2 * DB;
 
   // ---------------------------------------------------------------- softmax state
   const float c = p.scale_log2;
@@ -316,8 +353,8 @@ fwd_wide_kernel(FwdParams p) {
   };
   auto top = [&](int r) {
     if (!BAR2 || (r & 1) == 0) top_wait();
-    issue(Kp, r + KLA, kbuf(r + KLA), kdma);
-    issue(Vp, r + VLA, vbuf(r + VLA), vdma);
+    issue(Kp, r + KLA, kbuf(r + KLA), kdma, false);
+    issue(Vp, r + VLA, vbuf(r + VLA), vdma, true);
   };
 
   // One iteration.  HS: S_t is computed (t < n_w); HP: tile
@@ -380,8 +417,8 @@ fwd_wide_kernel(FwdParams p) {
     Copy kc{}, vc{};
     if constexpr (HS) {
       if (!BAR2 || (t & 1) == 0) top_wait();
-      kc = copy_of(Kp, t + KLA, kbuf(t + KLA));
-      vc = copy_of(Vp, t + VLA, vbuf(t + VLA));
+      kc = copy_of(Kp, t + KLA, kbuf(t + KLA), false);
+      vc = copy_of(Vp, t + VLA, vbuf(t + VLA), true);
     } else {
       top(t);
     }
@@ -419,7 +456,7 @@ fwd_wide_kernel(FwdParams p) {
         if constexpr (KK + 2 < KT) read_k(kst, ic<KK + 2>{});
         if constexpr (HP && KK == KT - 2) read_v(vst, ic<0>{});
         // LDS reads issued after k-step KK: up to two k-steps, and V chunk 0
-        constexpr int LEFT = 2 * ((KK + 2 < KT ? KK + 2 : KT - 1) - KK) + ((HP && KK >= KT - 2) ? 2 * DB : 0);
+        constexpr int LEFT = 2 * ((KK + 2 < KT ? KK + 2 : KT - 1) - KK) + ((HP && KK >= KT - 2) ? VREADS : 0);
         lgkm_wait<LEFT>();
         // MFMA (bb, qb), each with its share of the exponentials after it
         // (the scheduling barriers keep each group behind its MFMA)
@@ -487,7 +524,7 @@ fwd_wide_kernel(FwdParams p) {
         constexpr int C = CC & 1;
         if constexpr (CC + 1 < NC) {
           read_v(vst, ic<CC + 1>{});
-          lgkm_wait<2 * DB>();
+          lgkm_wait<VREADS>();
         } else {
           lgkm_wait<0>();
         }
@@ -547,8 +584,8 @@ fwd_wide_kernel(FwdParams p) {
   // the same number of copies)
 #pragma unroll
   for (int r = -KLA; r < 0; ++r) {
-    issue(Kp, r + KLA, kbuf(r + KLA), kdma);
-    issue(Vp, r + VLA >= 0 ? r + VLA : ntile, vbuf(r + VLA), vdma);
+    issue(Kp, r + KLA, kbuf(r + KLA), kdma, false);
+    issue(Vp, r + VLA >= 0 ? r + VLA : ntile, vbuf(r + VLA), vdma, true);
   }
   f32x16 s0[QB][NB], s1[QB][NB];
   vec8 p0[QB][NC], p1[QB][NC];
@@ -612,13 +649,13 @@ fwd_wide_kernel(FwdParams p) {
   }
 }
 
-template <typename T, bool CAUSAL, bool H4>
+template <typename T, bool CAUSAL, bool H4, bool VCOL>
 static hipError_t launch_wide_one(const FwdParams& p, hipStream_t s) {
   constexpr int lds = 2 * ATTN_WIDE_STAGES * 64 * 128 * 2;   // K and V rings of 16 KiB tiles
-  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_wide_kernel<T, CAUSAL, H4>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_wide_kernel<T, CAUSAL, H4, VCOL>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fwd_wide_kernel<T, CAUSAL, H4>), dim3(p.grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((fwd_wide_kernel<T, CAUSAL, H4, VCOL>), dim3(p.grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
@@ -626,21 +663,24 @@ static hipError_t launch_wide_one(const FwdParams& p, hipStream_t s) {
 #define ATTN_WIDE_HEADS4 1
 #endif
 
-template <typename T>
+template <typename T, bool VCOL>
 static hipError_t launch_wide_t(const FwdParams& p, int causal, hipStream_t s) {
   if (ATTN_WIDE_HEADS4 && p.group % 4 == 0) {
     // four query heads of one KV head per workgroup, 64 rows each
     FwdParams q = p;
     q.tm = make_tile_map(p.B, p.Hq / 4, p.Hkv, p.Sq, 64, causal);
     q.grid = q.tm.ntiles;
-    return causal ? launch_wide_one<T, true, true>(q, s) : launch_wide_one<T, false, true>(q, s);
+    return causal ? launch_wide_one<T, true, true, VCOL>(q, s) : launch_wide_one<T, false, true, VCOL>(q, s);
   }
-  return causal ? launch_wide_one<T, true, false>(p, s) : launch_wide_one<T, false, false>(p, s);
+  return causal ? launch_wide_one<T, true, false, VCOL>(p, s) : launch_wide_one<T, false, false, VCOL>(p, s);
 }
 
+// p.feat: 0, or kFeatVCol (column-major V); the tile map is the dense one of
+// 256-row blocks (or the head-packed one, chosen here)
 hipError_t launch_fwd_wide(const FwdParams& p, int dtype, int causal, hipStream_t s) {
-  if (dtype == 0) return launch_wide_t<__bf16>(p, causal, s);
-  return launch_wide_t<_Float16>(p, causal, s);
+  const bool vcol = (p.feat & kFeatVCol) != 0;
+  if (dtype == 0) return vcol ? launch_wide_t<__bf16, true>(p, causal, s) : launch_wide_t<__bf16, false>(p, causal, s);
+  return vcol ? launch_wide_t<_Float16, true>(p, causal, s) : launch_wide_t<_Float16, false>(p, causal, s);
 }
 
 }  // namespace attn

@@ -181,6 +181,19 @@ __device__ __forceinline__ void v_read(uint32_t addr) {
   asm volatile((v_read_text<C, DB, OFF, OFF2>())::"v"(addr));
 }
 
+// V fragment (c, db) from a column-major V tile: one plain 16-byte read of
+// 8 consecutive keys of one channel row
+template <int C, int DB, int OFF>
+constexpr Asm vcol_read_text() {
+  Asm t;
+  t.s("ds_read_b128 ").a(v_reg(C, DB), 4).s(", %0 offset:").i(OFF);
+  return t;
+}
+template <int C, int DB, int OFF>
+__device__ __forceinline__ void vcol_read(uint32_t addr) {
+  asm volatile((vcol_read_text<C, DB, OFF>())::"v"(addr));
+}
+
 // at most N LDS operations outstanding
 template <int N>
 __device__ __forceinline__ void lgkm_wait() {

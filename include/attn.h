@@ -184,7 +184,10 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
  *   aligned rows).
  * With both options off the call is attn_fwd.  With either on: dense
  * (cu_seqlens NULL) and dtype ATTN_BF16 / ATTN_FP16 only (else
- * ATTN_ERR_ARG); 128-row tiles of the 4-wave kernel.  Other arguments,
+ * ATTN_ERR_ARG).  Column-major V alone at d = 128 runs the one-wave-per-SIMD
+ * kernel of attn_fwd (its V tile then comes straight from the column-major
+ * layout); softcap, and d = 64, run 128-row tiles of the 4-wave kernel.
+ * Other arguments,
  * layouts and errors as attn_fwd.
  */
 int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
