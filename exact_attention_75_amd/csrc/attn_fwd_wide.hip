@@ -164,33 +164,48 @@ fwd_wide_kernel(FwdParams p) {
   static_assert(!VCOL || BN * 2 == 8 * 16, "V^T tile rows of 8 chunks");
   // column-major V: this (batch, KV head)'s [D, Sk] plane
   const T* Vt = VCOL ? (const T*)p.v + ((long long)b * p.Hkv + hkv) * D * p.Sk : nullptr;
-  // the copies of tile t of K or V into ring buffer buf: source, size and
-  // destination, all wave-uniform
+  // the copies of one K or V tile: source, size and destination, all
+  // wave-uniform
   struct Copy {
     const void* src;
     uint32_t bytes;
     char* dst;
   };
-  auto copy_of = [&](const T* base, int t, char* buf, bool is_v) {
-    const bool live = t < ntile;
-    const int j0 = live ? t * BN : 0;
-    if (VCOL && is_v) {
-      // range to the end of the plane: keys past Sk read the next channel's
-      // (finite) values, or zeros past the plane; their P is 0
-      return Copy{(const void*)(Vt + j0), live ? (uint32_t)(D * p.Sk - j0) * 2u : 0u, buf + wave * LOADS * 1024};
-    }
-    return Copy{(const void*)(base + (long long)j0 * ks),
-                live ? (uint32_t)(kv_len - j0) * (uint32_t)ks * 2u : 0u, buf + wave * LOADS * 1024};
+  // K tiles 0, 1, 2, ... and V tiles 0, 1, 2, ... go out in order, so each
+  // tensor keeps a running copy state (a few scalar adds per tile instead of
+  // a 64-bit address product and a branch): the address of its next tile,
+  // the bytes from there to the end of its range, the keys from the tile's
+  // first key to kv_end (none left: the copy gets an empty range and writes
+  // zeros) and the ring slot.  The range of a row-major tensor ends at
+  // kv_end: keys from there to the tile's end read zeros, and every row of
+  // the workgroup masks them.  The column-major V plane's range ends at the
+  // plane's end: keys past Sk read the next channel's (finite) values, or
+  // zeros past the plane; their P is 0.
+  struct Stream {
+    uint64_t src;
+    uint32_t bytes;
+    uint32_t step;
+    int keys;
+    int slot;
   };
-  auto issue = [&](const T* src, int t, char* buf, const uint32_t(&off)[LOADS], bool is_v) {
-    const Copy cp = copy_of(src, t, buf, is_v);
+  Stream ks_k{(uint64_t)(uintptr_t)Kp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
+  Stream ks_v = VCOL ? Stream{(uint64_t)(uintptr_t)Vt, (uint32_t)(D * p.Sk) * 2u, (uint32_t)(BN * 2), kv_end, 0}
+                     : Stream{(uint64_t)(uintptr_t)Vp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
+  auto next_copy = [&](Stream& st, int ring) {
+    const Copy cp{(const void*)(uintptr_t)st.src, st.keys > 0 ? st.bytes : 0u,
+                  smem + (ring + st.slot) * TILE + wave * LOADS * 1024};
+    st.src += st.step;
+    st.bytes -= st.step;
+    st.keys -= BN;
+    st.slot = st.slot + 1 == STAGES ? 0 : st.slot + 1;
+    return cp;
+  };
+  auto issue_copy = [&](const Copy& cp, const uint32_t(&off)[LOADS]) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) copy_row_to_lds(cp.src, cp.bytes, cp.dst + i * 1024, off[i]);
   };
   // ring slot of tile t (t >= -1)
   auto slot_of = [&](int t) { return (t + STAGES) % STAGES; };
-  auto kbuf = [&](int t) { return smem + slot_of(t) * TILE; };
-  auto vbuf = [&](int t) { return smem + (STAGES + slot_of(t)) * TILE; };
 
   // ---------------------------------------------------------------- LDS reads
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)smem;
@@ -266,10 +281,13 @@ fwd_wide_kernel(FwdParams p) {
 
   // mask: element i of s[qb][bb] is key j0 + 32 bb + 16 (i/8) + 8 h + i%8 for
   // query qw + 32 qb + l32
+  // Tile t needs the mask when it reaches past the last key (t BN + BN >
+  // kv_len) or, causal, past the wave's first row (t BN + BN - 1 > qw); both
+  // hold from some t on, so one comparison with the first such t decides.
+  const int t_edge = CAUSAL ? min(kv_len / BN, (qw + 1) / BN) : kv_len / BN;
   auto mask = [&](int t, f32x16(&sn)[QB][NB]) {
     const int j0 = t * BN;
-    const bool edge = (j0 + BN > kv_len) || (CAUSAL && j0 + BN - 1 > qw);
-    if (edge) {
+    if (t >= t_edge) {
       // (an opaque statement keeps this rare block a branch instead of
       // selects executed on every tile)
       asm volatile("" ::: "memory");
@@ -353,8 +371,8 @@ fwd_wide_kernel(FwdParams p) {
   };
   auto top = [&](int r) {
     if (!BAR2 || (r & 1) == 0) top_wait();
-    issue(Kp, r + KLA, kbuf(r + KLA), kdma, false);
-    issue(Vp, r + VLA, vbuf(r + VLA), vdma, true);
+    issue_copy(next_copy(ks_k, 0), kdma);
+    issue_copy(next_copy(ks_v, STAGES), vdma);
   };
 
   // One iteration.  HS: S_t is computed (t < n_w); HP: tile
@@ -417,8 +435,8 @@ fwd_wide_kernel(FwdParams p) {
     Copy kc{}, vc{};
     if constexpr (HS) {
       if (!BAR2 || (t & 1) == 0) top_wait();
-      kc = copy_of(Kp, t + KLA, kbuf(t + KLA), false);
-      vc = copy_of(Vp, t + VLA, vbuf(t + VLA), true);
+      kc = next_copy(ks_k, 0);         // K_{t+KLA}
+      vc = next_copy(ks_v, STAGES);    // V_{t+VLA}
     } else {
       top(t);
     }
@@ -584,8 +602,9 @@ fwd_wide_kernel(FwdParams p) {
   // the same number of copies)
 #pragma unroll
   for (int r = -KLA; r < 0; ++r) {
-    issue(Kp, r + KLA, kbuf(r + KLA), kdma, false);
-    issue(Vp, r + VLA >= 0 ? r + VLA : ntile, vbuf(r + VLA), vdma, true);
+    issue_copy(next_copy(ks_k, 0), kdma);
+    if (r + VLA >= 0) issue_copy(next_copy(ks_v, STAGES), vdma);
+    else issue_copy(Copy{Kp, 0u, smem + (STAGES + slot_of(r + VLA)) * TILE + wave * LOADS * 1024}, vdma);
   }
   f32x16 s0[QB][NB], s1[QB][NB];
   vec8 p0[QB][NC], p1[QB][NC];
