@@ -218,6 +218,27 @@ def test_varlen_small(ea, dtype, d):
         compare(o, lse, o_ref, l_ref, f"varlen {dtype} d{d} c{int(causal)}")
 
 
+@pytest.mark.parametrize("case", ["many_sequences", "long_sequence"])
+def test_varlen_block_order_fallbacks(ea, case):
+    # The kernel ranks (sequence, block) entries longest first when there are
+    # at most 64 sequences of at most 64 blocks; beyond that it walks the
+    # batch in order.  Both sides of that limit, every row compared.
+    if case == "many_sequences":
+        lengths = [int(x) for x in np.random.default_rng(3).integers(0, 300, 70)]
+        Hq, Hkv, d = 2, 1, 64
+    else:
+        lengths = [8321, 300, 5, 129]          # 66 blocks of 128 rows in the first
+        Hq, Hkv, d = 1, 1, 64
+    print(f"[case] varlen {case} B={len(lengths)} T={sum(lengths)}", flush=True)
+    q, k, v, cu = W.make_varlen(lengths, Hq, Hkv, d, "fp16", seed=17)
+    for causal in (False, True):
+        o, lse = ea.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                        cu_seqlens=torch.from_numpy(cu).cuda())
+        torch.cuda.synchronize()
+        o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), causal, cu_seqlens=cu)
+        compare(o, lse, o_ref, l_ref, f"varlen {case} c{int(causal)}")
+
+
 # ---------------------------------------------------------------- the five workloads
 def sampled_rows(S, n=40, seed=0):
     rng = np.random.default_rng(seed)
