@@ -36,10 +36,11 @@
 //    fixed head-dim column; ds_read_b64_tr_b16 (gfx950's transposing LDS
 //    read) delivers that from the row-major V tile.
 //  * Online softmax in the exp2 domain with scale*log2(e) folded into one
-//    FMA, and a lazy rescale: the running max is only moved (and O, l
-//    rescaled) when a row's new max exceeds it by more than 2^8 in
-//    probability, which is exact arithmetic (any reference point cancels in
-//    O = sum P V / sum P) and keeps P <= 256.
+//    FMA, and a lazy running max without a per-tile row max: the first tile
+//    takes the exact max, later probabilities are taken against it and their
+//    sum is checked against a bound before they enter the second GEMM; only
+//    when a sum exceeds it does the max move (and O, l get rescaled).  Exact
+//    arithmetic: any reference point cancels in O = sum P V / sum P.
 //  * Causal: a wave skips key tiles entirely above its diagonal; only tiles
 //    that cross the diagonal or the sequence end are masked (the pages' split
 //    loop, Hopper tag page contents 4.7).
@@ -93,7 +94,6 @@ fwd_kernel(FwdParams p) {
   // to itself (copies run two tiles ahead), two otherwise
   constexpr int STAGES = (NW == 8) ? 3 : 2;
   constexpr int LOADS = BN * CPR / (NW * 64);   // DMA instructions per wave per tile
-  constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
   constexpr float NEG_INF = -__builtin_inff();
   static_assert(BN == 64 && (BN * CPR) % (NW * 64) == 0, "tile shape");
   static_assert(!(PACK && VARLEN), "PackGQA is for dense inputs");
@@ -349,6 +349,7 @@ fwd_kernel(FwdParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   float m_run = NEG_INF;   // running max of scale*log2(e)*s for the lane's query (same in both halves)
+  float msub = 0.f;        // m_run, or 0 while it is -inf: the exponent offset of the probabilities
   // This lane half's share of the running sum of P, taken over the fp32
   // probabilities: bf16 keeps 8 significant bits, so summing the rounded
   // values could be off by 2^-9 relative, a 2e-3 error in LSE.
@@ -386,24 +387,23 @@ fwd_kernel(FwdParams p) {
   // every stretch of MFMAs below carries its share of the softmax:
   //   A: S_{t+1} = K_{t+1} Q^T (16 MFMA)   with  exp2 of S_t, chunks 0-1
   //   B: P_t V_t, chunks 0-1 (8 MFMA)      with  exp2 of S_t, chunks 2-3
-  //   C: P_t V_t, chunks 2-3 (8 MFMA)      with  mask + row max of S_{t+1}
-  // The probabilities are computed in place over S_t and packed into P.
+  //   C: P_t V_t, chunks 2-3 (8 MFMA)
+  // with the mask of S_{t+1} between A and B and the sum check of each chunk
+  // pair before its MFMAs.  The probabilities go straight into the packed
+  // operand P; S_t keeps the raw scores.
 
-  // exp2(c*s - m) in place for elements [e0, e0+n) of 16-key chunk cc
-  auto exps = [&](f32x16 (&sc)[NB], float msub, int cc, int e0, int n, float& rs) {
+  // P = exp2(c s - m) for elements [e0, e0+n) of 16-key chunk cc, into the
+  // second GEMM's operand pc and the sum rs; S keeps the raw scores (the
+  // rare rescale below needs them)
+  auto exps = [&](const f32x16 (&sc)[NB], int cc, int e0, int n, float& rs, vec8 (&pc)[NC]) {
 #pragma unroll
     for (int e = e0; e < e0 + n; ++e) {
-      const int i = 8 * (cc & 1) + e;
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc >> 1][i], c, -msub));
-      sc[cc >> 1][i] = x;
-      rs += x;
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cc >> 1][8 * (cc & 1) + e], c, -msub));
       keep(x);
+      rs += x;
+      pc[cc][e] = (T)x;
     }
-  };
-  auto pack = [&](f32x16 (&sc)[NB], int cc, vec8 (&pc)[NC]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pc[cc][e] = (T)sc[cc >> 1][8 * (cc & 1) + e];
-    keep_vec(pc[cc]);
+    if (e0 + n == 8) keep_vec(pc[cc]);
   };
   // mask: element i of block bb is key j0 + 32*bb + 16*(i/8) + 8*h + i%8
   auto mask = [&](int t, f32x16 (&sn)[NB]) {
@@ -431,23 +431,46 @@ fwd_kernel(FwdParams p) {
         }
     }
   };
-  // row max over the lane's 32 keys, then across the two lane halves, and the
-  // lazy rescale: the running max only moves (by a wave-uniform decision)
-  // when some row's max exceeds it by more than 2^TAU in probability
-  float msub = 0.f, alpha_next = 1.f;
-  auto finish_max = [&](float mx) {
-    mx = fmaxf(mx, wave_half_swap(mx));
-    const float m_new = fmaxf(m_run, mx * c);
-    const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0;
-    const float m_upd = moved ? m_new : m_run;
-    alpha_next = (m_upd == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_upd);
-    m_run = m_upd;
-    msub = (m_run == NEG_INF) ? 0.f : m_run;
-  };
+  // Running max without a per-tile row max.  The first tile sets m to its
+  // exact row max.  After that each tile's probabilities are taken against
+  // the current m, and before a pair of 16-key chunks enters the second GEMM
+  // each lane's share of the pair's sum is compared with PMAX: the sum bounds
+  // every probability of the pair, so in the common case P <= PMAX (far
+  // inside the fp32, bf16 and fp16 ranges) and nothing else is needed.  When
+  // some lane exceeds it (or a sum is not finite) the wave takes a rare
+  // branch: m moves to the tile's row max (its raw scores are still in
+  // registers), O and l are rescaled by 2^(m_old - m_new) and the pair's
+  // probabilities are recomputed.  Any reference point cancels in
+  // O = sum P V / sum P, so the result is the same exact arithmetic.
+  constexpr float PMAX = 16384.0f;
   auto max16 = [&](const f32x16& x, float mx) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);   // chains into v_max3
     return mx;
+  };
+  auto first_max = [&](const f32x16 (&sc)[NB]) {
+    float mx = NEG_INF;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) mx = max16(sc[bb], mx);
+    mx = fmaxf(mx, wave_half_swap(mx));
+    m_run = mx * c;
+    msub = (m_run == NEG_INF) ? 0.f : m_run;
+  };
+  // rare: move m to the row max of tile sc; returns the factor applied to O
+  // and l (the caller rescales its own partial sums)
+  auto move_max = [&](const f32x16 (&sc)[NB]) {
+    float mx = NEG_INF;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) mx = max16(sc[bb], mx);
+    mx = fmaxf(mx, wave_half_swap(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float a = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= a;
+    l_run *= a;
+    m_run = m_new;
+    msub = (m_new == NEG_INF) ? 0.f : m_new;
+    return a;
   };
 
   // Operand reads for k-step kk: K of both 32-key blocks, and Q when it lives
@@ -481,14 +504,7 @@ fwd_kernel(FwdParams p) {
   // transposing V reads run one 16-key chunk ahead of their MFMAs (chunk 0 is
   // issued near the end of stretch A, when the K prefetch registers free up).
   auto tile = [&](int t, bool has_next, f32x16 (&sc)[NB], f32x16 (&sn)[NB]) {
-    // O and l pick up the rescale owed to tile t's max (a rare branch for O)
-    if (__builtin_amdgcn_ballot_w64(alpha_next != 1.f) != 0) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha_next;
-    }
-    l_run *= alpha_next;
-    const float ms = msub;
-    float rs = 0.f;
+    float rs01 = 0.f, rs23 = 0.f;   // lane shares of the sums of chunks 0-1 and 2-3
     vec8 pc[NC];
     const uint32_t vst = (t % STAGES) * TILE;
     i16x4 vr0[2 * DB], vr1[2 * DB], vr2[2 * DB], vr3[2 * DB];
@@ -515,16 +531,21 @@ fwd_kernel(FwdParams p) {
         for (int bb = 0; bb < NB; ++bb) sn[bb] = Mma<T>::run(kr[kk % 3][bb], qv[kk % 3], sn[bb]);
         // 16 exponentials spread over the KT k-steps
         constexpr int PER = 16 / KT;
-        exps(sc, ms, (kk * PER) / 8, (kk * PER) % 8, PER, rs);
-        if (((kk + 1) * PER) % 8 == 0) pack(sc, ((kk + 1) * PER) / 8 - 1, pc);
+        exps(sc, (kk * PER) / 8, (kk * PER) % 8, PER, rs01, pc);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       read_v(vr0, vst, std::integral_constant<int, 0>{});
-      exps(sc, ms, 0, 0, 8, rs);
-      exps(sc, ms, 1, 0, 8, rs);
-      pack(sc, 0, pc);
-      pack(sc, 1, pc);
+      exps(sc, 0, 0, 8, rs01, pc);
+      exps(sc, 1, 0, 8, rs01, pc);
+    }
+    // chunks 0-1 enter the second GEMM next: their sum check
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs01 <= PMAX)) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      move_max(sc);
+      rs01 = 0.f;
+      exps(sc, 0, 0, 8, rs01, pc);
+      exps(sc, 1, 0, 8, rs01, pc);
     }
 
     // S_{t+1} is complete: mask it now (rare branch, outside the stretches)
@@ -532,45 +553,48 @@ fwd_kernel(FwdParams p) {
 
     // ---- B: chunks 0-1 of P V, exp2 of chunks 2-3
     read_v(vr1, vst, std::integral_constant<int, 1>{});
-    exps(sc, ms, 2, 0, 4, rs);
+    exps(sc, 2, 0, 4, rs23, pc);
     lds_wait<2 * DB>(vr0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       mma_chunk(vr0, db, pc[0]);
-      exps(sc, ms, 2, 4 + db * (4 / DB), 4 / DB, rs);
+      exps(sc, 2, 4 + db * (4 / DB), 4 / DB, rs23, pc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    pack(sc, 2, pc);
     read_v(vr2, vst, std::integral_constant<int, 2>{});
-    exps(sc, ms, 3, 0, 4, rs);
+    exps(sc, 3, 0, 4, rs23, pc);
     lds_wait<2 * DB>(vr1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       mma_chunk(vr1, db, pc[1]);
-      exps(sc, ms, 3, 4 + db * (4 / DB), 4 / DB, rs);
+      exps(sc, 3, 4 + db * (4 / DB), 4 / DB, rs23, pc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    pack(sc, 3, pc);
-    l_run += rs;
+    // chunks 2-3: their sum check (O already holds chunks 0-1, taken against
+    // the old m: the rescale of O covers them, and of rs01 their sum)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs23 <= PMAX)) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      rs01 *= move_max(sc);
+      rs23 = 0.f;
+      exps(sc, 2, 0, 8, rs23, pc);
+      exps(sc, 3, 0, 8, rs23, pc);
+    }
+    l_run += rs01 + rs23;
 
-    // ---- C: chunks 2-3 of P V, row max of S_{t+1}
-    float mx = NEG_INF;
+    // ---- C: chunks 2-3 of P V
     read_v(vr3, vst, std::integral_constant<int, 3>{});
     lds_wait<2 * DB>(vr2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) mma_chunk(vr2, db, pc[2]);
-    if (has_next) mx = max16(sn[0], mx);
     __builtin_amdgcn_sched_barrier(0);
     lds_wait<0>(vr3);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db) mma_chunk(vr3, db, pc[3]);
-    if (has_next) mx = max16(sn[NB - 1], mx);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_next) finish_max(mx);
   };
 
   // tiles this wave computes (a causal wave stops at its diagonal; a wave
@@ -611,12 +635,7 @@ fwd_kernel(FwdParams p) {
   f32x16 sA[NB], sB[NB];
   s_alone(0, sA);
   mask(0, sA);
-  {
-    float mx = NEG_INF;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) mx = max16(sA[bb], mx);
-    finish_max(mx);
-  }
+  first_max(sA);
   int t = 0;
   for (; t + 2 < n_w; t += 2) {          // unrolled by two: the S sets swap roles
     top(t + 1);
