@@ -154,10 +154,13 @@ struct Mma<_Float16> {
 
 // Swizzle of 16-byte chunks inside one LDS row of the K tile: chunk c of row
 // r is stored at position c ^ swz_k(r).  16 consecutive rows (the lanes that
-// read one chunk column together) land on 16 different chunk positions.
+// read one chunk column together) land on 16 different 16-byte bank groups
+// of the 256-byte bank space: a 256-byte row has 16 chunk positions; a
+// 128-byte row puts odd rows in the upper half, so rows r and r ^ 1 share a
+// position and r >> 1 picks it.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return (D == 128) ? (r & 15) : (r & 7);
+  return (D == 128) ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Swizzle of the V tile.  A transposing read covers 4 consecutive rows x 64
