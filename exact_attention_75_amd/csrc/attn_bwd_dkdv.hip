@@ -99,16 +99,26 @@ bwd_dkdv_kernel(BwdParams p) {
   if constexpr (VARLEN) {
     hkv = blockIdx.x % p.Hkv;
     int r = blockIdx.x / p.Hkv, sq = 0, start = 0, len = 0;
-    for (; sq < p.B; ++sq) {
-      start = p.cu_seqlens[sq];
-      len = p.cu_seqlens[sq + 1] - start;
-      const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
-      if (r < nb) break;
-      r -= nb;
+    // longest blocks first over the whole batch: causal, key block j of nb
+    // is seen by the queries from j on, level nb - 1 - j
+    VarlenEntry ve;
+    if (varlen_rank<kBwdBlockN, CAUSAL>(p.cu_seqlens, p.B, r, ve)) {
+      if (ve.seq < 0) return;             // beyond the last block (uniform over the workgroup)
+      start = ve.start;
+      len = ve.len;
+      nblk = CAUSAL ? (len + kBwdBlockN - 1) / kBwdBlockN - 1 - ve.level : ve.level;
+    } else {
+      for (; sq < p.B; ++sq) {
+        start = p.cu_seqlens[sq];
+        len = p.cu_seqlens[sq + 1] - start;
+        const int nb = (len + kBwdBlockN - 1) / kBwdBlockN;
+        if (r < nb) break;
+        r -= nb;
+      }
+      if (sq >= p.B) return;              // beyond the last block (uniform over the workgroup)
+      nblk = r;
     }
-    if (sq >= p.B) return;                // beyond the last block (uniform over the workgroup)
     b = 0;
-    nblk = r;
     q_len = k_len = len;
     q_tok0 = k_tok0 = start;
   } else {

@@ -86,16 +86,25 @@ bwd_dq_pipe_kernel(BwdParams p) {
   if constexpr (VARLEN) {
     hq = blockIdx.x % p.Hq;
     int r = blockIdx.x / p.Hq, sq = 0, start = 0, len = 0, nb = 0;
-    for (; sq < p.B; ++sq) {
-      start = p.cu_seqlens[sq];
-      len = p.cu_seqlens[sq + 1] - start;
-      nb = (len + kBwdBlockM - 1) / kBwdBlockM;
-      if (r < nb) break;
-      r -= nb;
+    // longest blocks first over the whole batch (level = query block index)
+    VarlenEntry ve;
+    if (varlen_rank<kBwdBlockM, CAUSAL>(p.cu_seqlens, p.B, r, ve)) {
+      if (ve.seq < 0) return;             // beyond the last block (uniform over the workgroup)
+      mblk = ve.level;
+      start = ve.start;
+      len = ve.len;
+    } else {
+      for (; sq < p.B; ++sq) {
+        start = p.cu_seqlens[sq];
+        len = p.cu_seqlens[sq + 1] - start;
+        nb = (len + kBwdBlockM - 1) / kBwdBlockM;
+        if (r < nb) break;
+        r -= nb;
+      }
+      if (sq >= p.B) return;              // beyond the last tile (uniform over the workgroup)
+      mblk = nb - 1 - r;                  // longest query block of the sequence first
     }
-    if (sq >= p.B) return;                // beyond the last tile (uniform over the workgroup)
     b = 0;
-    mblk = nb - 1 - r;                    // longest query block of the sequence first
     q_len = k_len = len;
     q_tok0 = k_tok0 = start;
     stat0 = (long long)hq * p.Sq + start; // varlen layout [Hq, T]

@@ -127,56 +127,15 @@ fwd_kernel(FwdParams p) {
     hq = pid % p.Hq;
     int r = pid / p.Hq;        // rank of the workgroup's (sequence, block) entry
     int s = -1, start = 0, len = 0;
-    bool ranked = false;
-    if (p.B <= 64) {
-      // Longest blocks first over the whole batch (the grid's tail then holds
-      // the short ones).  Lane l reads the bounds of sequence l.  Causal: a
-      // block with index m costs about m + 1 key tiles, so the entries run
-      // over block index m descending, sequences ascending within one m; lane
-      // m counts the entries with index >= m, and a ballot finds the index
-      // of rank r.  Full attention: every block of a sequence costs its
-      // length, so whole sequences go longest first; lane l ranks its
-      // sequence and sums the blocks of the sequences ranked before it.
-      const int c0 = lane < p.B ? p.cu_seqlens[lane] : 0;
-      const int c1 = lane < p.B ? p.cu_seqlens[lane + 1] : 0;
-      const int nb_l = (c1 - c0 + BM - 1) / BM;
-      if constexpr (CAUSAL) {
-        int cnt = 0, mx = 0;
-        for (int j = 0; j < p.B; ++j) {
-          const int nbj = __builtin_amdgcn_readlane(nb_l, j);
-          mx = max(mx, nbj);
-          cnt += max(0, nbj - lane);
-        }
-        if (mx <= 64) {
-          ranked = true;
-          const int m = __builtin_popcountll(__builtin_amdgcn_ballot_w64(cnt > r)) - 1;   // -1: no entry
-          if (m >= 0) {
-            const int k = r - (m + 1 < 64 ? __builtin_amdgcn_readlane(cnt, m + 1) : 0);
-            const bool has = lane < p.B && nb_l > m;
-            const uint64_t hb = __builtin_amdgcn_ballot_w64(has);
-            const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hb >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)hb, 0u));
-            s = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(has && below == k));
-            mblk = m;
-          }
-        }
-      } else {
-        int base = 0;
-        for (int j = 0; j < p.B; ++j) {
-          const int nbj = __builtin_amdgcn_readlane(nb_l, j);
-          base += (nbj > nb_l || (nbj == nb_l && j < lane)) ? nbj : 0;
-        }
-        ranked = true;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < p.B && r >= base && r < base + nb_l);
-        if (hit != 0) {
-          s = (int)__builtin_ctzll(hit);
-          mblk = r - __builtin_amdgcn_readlane(base, s);
-        }
-      }
-      if (ranked && s >= 0) {
-        start = __builtin_amdgcn_readlane(c0, s);
-        len = __builtin_amdgcn_readlane(c1, s) - start;
-      }
+    // longest blocks first over the whole batch (the grid's tail then holds
+    // the short ones); the level is the query block's index
+    VarlenEntry ve;
+    const bool ranked = varlen_rank<BM, CAUSAL>(p.cu_seqlens, p.B, r, ve);
+    if (ranked && ve.seq >= 0) {
+      s = ve.seq;
+      mblk = ve.level;
+      start = ve.start;
+      len = ve.len;
     }
     if (!ranked) {
       // many sequences, or one of more than 64 blocks: the batch's order,

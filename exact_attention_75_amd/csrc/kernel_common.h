@@ -152,6 +152,67 @@ struct Mma<_Float16> {
   }
 };
 
+// Ragged batches: the workgroup of rank r among the (sequence, block)
+// entries of a batch of B sequences packed by cu (blocks of BM rows), ranked
+// longest first.  Causal: a block at level m costs about m + 1 block-widths
+// of work (the query block m of the forward and of dQ, the key block
+// nb - 1 - m of dK/dV), so the entries run over m descending, sequences
+// ascending within one m; lane m counts the entries at level >= m and a
+// ballot finds the level of rank r.  Full attention: every block of a
+// sequence costs the sequence's length, so whole sequences go longest first
+// (ties by index) and level = the block's index in its sequence.  Lane l reads
+// sequence l's bounds (one coalesced load).  Handles up to 64 sequences of up
+// to 64 blocks and then returns true, with seq = -1 when r is past the last
+// entry; otherwise returns false and the caller walks the batch.  Results are
+// wave-uniform.
+struct VarlenEntry {
+  int seq, level, start, len;
+};
+template <int BM, bool CAUSAL>
+__device__ __forceinline__ bool varlen_rank(const int32_t* cu, int B, int r, VarlenEntry& e) {
+  if (B > 64) return false;
+  const int lane = threadIdx.x & 63;
+  const int c0 = lane < B ? cu[lane] : 0;
+  const int c1 = lane < B ? cu[lane + 1] : 0;
+  const int nb_l = (c1 - c0 + BM - 1) / BM;
+  e.seq = -1;
+  e.level = 0;
+  if constexpr (CAUSAL) {
+    int cnt = 0, mx = 0;
+    for (int j = 0; j < B; ++j) {
+      const int nbj = __builtin_amdgcn_readlane(nb_l, j);
+      mx = max(mx, nbj);
+      cnt += max(0, nbj - lane);
+    }
+    if (mx > 64) return false;
+    const int m = __builtin_popcountll(__builtin_amdgcn_ballot_w64(cnt > r)) - 1;   // -1: no entry
+    if (m >= 0) {
+      const int k = r - (m + 1 < 64 ? __builtin_amdgcn_readlane(cnt, m + 1) : 0);
+      const bool has = lane < B && nb_l > m;
+      const uint64_t hb = __builtin_amdgcn_ballot_w64(has);
+      const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hb, 0u));
+      e.seq = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(has && below == k));
+      e.level = m;
+    }
+  } else {
+    int base = 0;
+    for (int j = 0; j < B; ++j) {
+      const int nbj = __builtin_amdgcn_readlane(nb_l, j);
+      base += (nbj > nb_l || (nbj == nb_l && j < lane)) ? nbj : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && r >= base && r < base + nb_l);
+    if (hit != 0) {
+      e.seq = (int)__builtin_ctzll(hit);
+      e.level = r - __builtin_amdgcn_readlane(base, e.seq);
+    }
+  }
+  if (e.seq >= 0) {
+    e.start = __builtin_amdgcn_readlane(c0, e.seq);
+    e.len = __builtin_amdgcn_readlane(c1, e.seq) - e.start;
+  }
+  return true;
+}
+
 // Swizzle of 16-byte chunks inside one LDS row of the K tile: chunk c of row
 // r is stored at position c ^ swz_k(r).  16 consecutive rows (the lanes that
 // read one chunk column together) land on 16 different 16-byte bank groups

@@ -192,6 +192,30 @@ def test_bwd_varlen(ea, dtype, d, causal, lens):
     compare("dv", dv, rv, tag)
 
 
+@pytest.mark.parametrize("case", ["many_sequences", "long_sequence"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_block_order_fallbacks(ea, case, causal):
+    # Both backward kernels rank (sequence, block) entries longest first for
+    # at most 64 sequences of at most 64 blocks and walk the batch in order
+    # beyond that; both sides of the limit, every gradient element compared.
+    if case == "many_sequences":
+        lens = [int(x) for x in np.random.default_rng(4).integers(0, 200, 70)]
+        Hq, Hkv = 2, 1
+    else:
+        lens = [8321, 300, 5, 129]               # 66 blocks of 128 in the first
+        Hq, Hkv = 1, 1
+    print(f"[case] bwd varlen {case} causal={causal} B={len(lens)}", flush=True)
+    cu, q, k, v, do, o, lse = varlen_inputs(lens, Hq, Hkv, 64, "fp16", 77, causal)
+    dev = [t.cuda() for t in (q, k, v, o, lse, do)]
+    dq, dk, dv = ea.bwd(*dev, causal=causal, cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    rq, rk, rv = A.attention_backward(q, k, v, do, 1 / 8, causal, cu_seqlens=cu)
+    tag = f"bwd varlen {case} c{int(causal)}"
+    compare("dq", dq, rq, tag)
+    compare("dk", dk, rk, tag)
+    compare("dv", dv, rv, tag)
+
+
 def test_bwd_varlen_c4_sampled_heads(ea):
     # c4's packed batch (10 sequences, fp16, d = 64, causal): the GPU computes
     # every head, the oracle heads 0 and 15 over all sequences
