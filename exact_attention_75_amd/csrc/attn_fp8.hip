@@ -447,6 +447,10 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   const int n_w = CAUSAL ? min(ntile, (qw + 31) / BN + 1) : ntile;
 
   float msub = 0.f;
+  // factors of the current 128-key scale block, shared by the two tiles of
+  // an unrolled pair (t even, t + 1): formed in the first of them
+  float c = 0.f, lv = 0.f;
+  int vscale = 127;
   // One key tile: barrier, the next tile's copies, and -- for tiles this
   // wave computes -- S, the probabilities, the sum check and PV.  STAGE is
   // t % 2, a constant, so every LDS read is a per-lane base plus an
@@ -459,14 +463,16 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     const char* Ks = smem + STAGE * TILE;
     const char* Vs = smem + (2 + STAGE) * TILE;
     const int j0 = t * BN;
-    // block scales by scalar loads (a vector load would queue behind the
-    // copies in flight and make the tile wait for them)
-    const float c = cbase * ((const __attribute__((address_space(4))) float*)ksc)[j0 >> 7];
-    // V block ratio 2^lv = 2^(e + f): 2^e as the E8M0 scale of V (clamped at
-    // the format's 2^-127), 2^f in P'
-    const float lv_all = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;
-    const int vscale = max(0, 127 + (int)ceilf(lv_all));
-    const float lv = lv_all - (float)(vscale - 127);   // (-1, 0] unless clamped
+    if constexpr (STAGE == 0) {
+      // block scales by scalar loads (a vector load would queue behind the
+      // copies in flight and make the tile wait for them)
+      c = cbase * ((const __attribute__((address_space(4))) float*)ksc)[j0 >> 7];
+      // V block ratio 2^lv = 2^(e + f): 2^e as the E8M0 scale of V (clamped
+      // at the format's 2^-127), 2^f in P'
+      const float lv_all = log2f(((const __attribute__((address_space(4))) float*)vsc)[j0 >> 7]) - lsv_max;
+      vscale = max(0, 127 + (int)ceilf(lv_all));
+      lv = lv_all - (float)(vscale - 127);   // (-1, 0] unless clamped
+    }
 
     // ---- S^T = K Q^T.  Each MFMA group runs at raised wave priority: the
     // other wave on this SIMD (another workgroup's) is then mostly in its
