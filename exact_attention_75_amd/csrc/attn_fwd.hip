@@ -77,8 +77,18 @@ namespace attn {
 //                 innermost: the V_colmajor input, same page, FP8 layout
 //                 discussion): the PV operand is then a plain 16-byte read
 //                 of a V^T tile instead of a transposing read.
+// Waves per SIMD the register budget is set for: two, except for the causal
+// varlen d = 64 instance with 4 waves, whose 167 registers fit three (three
+// 4-wave workgroups per CU, 96 KiB of LDS): more waves resident over ragged
+// batches whose blocks vary in length.  The other d = 64 instances spill at
+// that budget.
+constexpr int fwd_waves_per_simd(int D, int NW, bool CAUSAL, bool VARLEN) {
+  return (NW == 4 && D == 64 && CAUSAL && VARLEN) ? 3 : 2;
+}
+
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT, bool PACK, int FEAT>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D, NW, CAUSAL, VARLEN), fwd_waves_per_simd(D, NW, CAUSAL, VARLEN))))
 fwd_kernel(FwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
   constexpr int NTHREADS = 64 * NW;
