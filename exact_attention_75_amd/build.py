@@ -70,19 +70,48 @@ PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip", "attn_bwd_dkdv.hip", "attn_bwd_dq.hi
 
 def check_pinned_agprs(src: str) -> None:
     """Compile `src` to device assembly and fail unless, in every kernel, AGPRs
-    appear only inside inline-assembly regions and nothing spills."""
+    appear only inside inline-assembly regions, nothing spills, and the kernel
+    descriptor allocates every AGPR the inline assembly names (the AGPRs of a
+    wave are the registers from .amdhsa_accum_offset up to
+    .amdhsa_next_free_vgpr; one named past that would belong to another
+    wave)."""
     asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
     cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"assembly listing failed: {src}\n{r.stderr}")
+    with open(asm) as f:
+        scan_pinned_agprs(src, f)
+
+
+def scan_pinned_agprs(src: str, lines) -> None:
+    """The checks of check_pinned_agprs over the lines of an assembly listing."""
     agpr = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
+    agpr_index = re.compile(r"\ba(\d+)\b|\ba\[\d+:(\d+)\]")
     in_asm = False
     kernel = None
-    for line in open(asm):
+    named = {}        # kernel -> highest AGPR index its inline assembly names
+    desc = None       # kernel whose descriptor is being read
+    fields = {}
+    for line in lines:
         if line.startswith("_Z") and line.rstrip().endswith(":"):
             kernel = line.split(":")[0]
+            named.setdefault(kernel, -1)
         t = line.strip()
+        if t.startswith(".amdhsa_kernel "):
+            desc, fields = t.split()[1], {}
+            continue
+        if desc is not None:
+            f = t.split()
+            if len(f) == 2 and f[0] in (".amdhsa_next_free_vgpr", ".amdhsa_accum_offset"):
+                fields[f[0]] = int(f[1])
+            if t.startswith(".end_amdhsa_kernel"):
+                top = named.get(desc, -1)
+                have = fields.get(".amdhsa_next_free_vgpr", 0) - fields.get(".amdhsa_accum_offset", 0)
+                if top >= have:
+                    raise RuntimeError(f"{src}: {desc} names a{top} but its descriptor allocates {have} AGPRs")
+                desc = None
+            continue
         if t.startswith(";;#ASMSTART"):
             in_asm = True
             continue
@@ -90,6 +119,9 @@ def check_pinned_agprs(src: str) -> None:
             in_asm = False
             continue
         code = t.split(";")[0]
+        if kernel and in_asm and code:
+            for m in agpr_index.finditer(code):
+                named[kernel] = max(named[kernel], int(m.group(1) or m.group(2)))
         if kernel and not in_asm and code and not code.startswith(".") and agpr.search(code):
             raise RuntimeError(f"{src}: compiler-generated AGPR use in {kernel}: {code}")
         m = re.match(r"\.(vgpr_spill_count|private_segment_fixed_size):\s+(\d+)", t)

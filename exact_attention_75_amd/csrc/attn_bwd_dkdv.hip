@@ -72,8 +72,15 @@ __device__ __forceinline__ void acc_zero() {
 // VARLEN: p.B sequences packed along the token axis (cu_seqlens); the
 // statistics are then read from global memory (their per-sequence rows are
 // not 16-byte aligned for the copy).
+// Register budget (waves per SIMD): d = 128 one; d = 64 three (the 96 named
+// AGPRs plus at most 72 VGPRs), except full attention over ragged batches,
+// whose instance needs 76 VGPRs and gets two.
+constexpr int dkdv_waves_per_simd(int D, bool CAUSAL, bool VARLEN) {
+  return D == 128 ? 1 : (!CAUSAL && VARLEN) ? 2 : 3;
+}
 template <typename T, int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(dkdv_waves_per_simd(D, CAUSAL, VARLEN), dkdv_waves_per_simd(D, CAUSAL, VARLEN))))
 bwd_dkdv_kernel(BwdParams p) {
   using namespace dkdv;
   typedef typename Mma<T>::vec8 vec8;
