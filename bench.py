@@ -271,7 +271,8 @@ def splitkv_leg(ea, name, steps, warmup):
             raise RuntimeError(L.attn_strerror(rc).decode())
 
     def plain():
-        rc = L.attn_fwd(*args, None, ea.ATTN_BF16, st)
+        # one key range: the unsplit kernel (attn_fwd itself splits this shape)
+        rc = L.attn_fwd_splitkv(*args, 1, -1, ea.ATTN_BF16, st)
         if rc != 0:
             raise RuntimeError(L.attn_strerror(rc).decode())
     ts = timed(split, steps, warmup)

@@ -97,6 +97,8 @@ int workspace(int kind, size_t bytes, hipStream_t s, void** out) {
 
 constexpr int kMaxSplits = attn::kCombineMaxSplits;
 constexpr int kSplitBlockM = 128;   // query rows per workgroup of the split / packed kernel
+constexpr long long kAutoSplitGrid = 128;   // attn_fwd considers split-KV below this many workgroups
+constexpr int kAutoSplitMinKeys = 4096;     // ... and from this many keys (shorter: the combine launch costs more)
 // PackGQA (one tile holds the rows of every query head of a KV group) needs
 // the group size to divide the 128-row block.  Automatic choice: pack when it
 // gives strictly fewer 128-row tiles, i.e. when the unpacked tiles would be
@@ -436,7 +438,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     int pack = 0;
     rc = pack_choice(-1, Hq, Hkv, Sq, &pack);
     if (rc) return rc;
-    return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, 1, 0, dtype, s);
+    // Few query blocks over long keys (decoding): when the plain launch
+    // would occupy under half the CUs and there are at least 4096 keys, cut
+    // the key axis as attn_fwd_splitkv does if its planner finds that faster.
+    const long long plain = pack ? dense_tiles(B, Hq, Hkv, Sq, 1)
+                                 : (long long)B * Hq * ((Sq + attn::fwd_block_m(dtype, d, 0) - 1) /
+                                                        attn::fwd_block_m(dtype, d, 0));
+    int splits = 1, split_keys = 0;
+    if (plain < kAutoSplitGrid && Sk >= kAutoSplitMinKeys) {
+      rc = split_plan(dense_tiles(B, Hq, Hkv, Sq, pack), Sk, d, 0, &splits, &split_keys);
+      if (rc) return rc;
+    }
+    return fwd16_dense(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, pack, splits, split_keys, dtype, s);
   }
   attn::FwdParams p{};
   fill_params(p, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale);

@@ -100,7 +100,14 @@ enum attn_status {
  *   (1/sqrt(d) gives the formula's 1/sqrt(d_k)).
  * causal: non-zero hides key j from query i when j > i.
  * bf16/fp16 dense calls with GQA and few query positions use PackGQA (see
- *   attn_fwd_splitkv); the result does not depend on that choice.
+ *   attn_fwd_splitkv); the result does not depend on that choice.  When the
+ *   plain launch would hold fewer than 128 workgroups and Sk >= 4096 (few
+ *   query blocks over a long key cache, e.g. decoding), the call runs attn_fwd_splitkv's
+ *   plan (num_splits = 0) and, if that plan cuts the keys, its split-KV
+ *   partials and combine: O and LSE agree with the plain path to rounding,
+ *   and the call then uses the split-KV workspace (shared with
+ *   attn_fwd_splitkv; such calls on different streams of one device must
+ *   not overlap).
  * dtype: an attn_dtype.  For the fp8 types q, k, v are fp32 and o is bf16;
  *   the quantised copies live in a library-owned, lazily grown device
  *   workspace (released by attn_release; fp8 calls on different streams of

@@ -148,6 +148,22 @@ def test_splitkv_decode_shape(ea):
             compare(o, lse, o_ref, l_ref, f"splitkv decode c{int(causal)} pack{pack}")
 
 
+def test_fwd_splits_the_decode_shape(ea):
+    # attn_fwd on a decode shape (the plain launch would hold 32 workgroups,
+    # 16384 keys) follows attn_fwd_splitkv's own plan: the same kernels, so
+    # the same bits; a shape with a full grid keeps the plain kernel
+    B, Sq, Sk, Hq, Hkv, d = 4, 1, 16384, 32, 8, 128
+    q, k, v = W.make_dense(B, Sq, Sk, Hq, Hkv, d, "bf16", seed=16)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = ea.fwd(qc, kc, vc)
+    o2, l2 = ea.fwd_splitkv(qc, kc, vc, num_splits=0)
+    torch.cuda.synchronize()
+    assert ea.split_plan(B, Hq, Hkv, Sq, Sk, d=d)[0] > 1
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(d), False)
+    compare(o1, l1, o_ref, l_ref, "attn_fwd decode shape")
+
+
 def test_splitkv_one_range_is_the_plain_forward(ea):
     q, k, v = W.make_dense(1, 300, 300, 2, 2, 64, "fp16", seed=13)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
