@@ -133,9 +133,10 @@ long long dense_tiles(int B, int Hq, int Hkv, int Sq, int pack) {
 // time as (waves of workgroups over the device's resident slots) x (work of
 // one workgroup: its share of the keys plus a fixed cost worth 128 keys) and
 // takes the cheapest count, the smallest on ties, with ranges of at least
-// 256 keys and at most 64 ranges.  Slots: 256 CUs (MI355X) times the
-// workgroups of the 4-wave kernel one CU holds (one with d = 128, whose K/V
-// ring and Q block take 96 KiB of LDS; two with d = 64).
+// 256 keys and at most 64 ranges.  Slots: 256 CUs (MI355X) times one
+// (d = 128) or two (d = 64) workgroups of the 4-wave kernel.  At d = 128 two
+// workgroups fit in a CU's LDS, but the count of one matches what the decode
+// shape measures best (8 ranges 43.8 us against 16 ranges 49.8 us).
 int split_plan(long long tiles, int Sk, int d, int num_splits, int* splits, int* split_keys) {
   if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_ARG;
   const int kt = (Sk + 63) / 64;   // 64-key tiles

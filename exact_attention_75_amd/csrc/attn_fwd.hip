@@ -114,9 +114,14 @@ fwd_kernel(FwdParams p) {
   // With d = 128 the Q block lives in LDS (its 32 registers per lane are
   // needed by the pipeline); with d = 64 it stays in registers.
   constexpr bool QLDS = (D == 128);
-  // [K stages | V stages | Q block (QLDS)]
+  // d = 128 with 4 waves: one K buffer instead of two (80 KiB of LDS in all,
+  // so two workgroups share a CU): the next K tile is copied once every wave
+  // has finished stretch A of the current one, behind a second barrier.
+  constexpr bool KSINGLE = QLDS && NW == 4;
+  constexpr int KST = KSINGLE ? 1 : STAGES;   // K buffers
+  // [K buffers | V stages | Q block (QLDS)]
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const qsm = smem + 2 * STAGES * TILE;
+  char* const qsm = smem + (KST + STAGES) * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -301,7 +306,7 @@ fwd_kernel(FwdParams p) {
     const int dd = 16 * (G & 1) + 4 * (i16 & 3);
     voff0 = r * ROW + ((((dd >> 3) ^ swz_v<D>(r))) << 4) + ((dd & 7) << 1);
   }
-  auto voff = [&](int db) { return (voff0 ^ (uint32_t)(db << 6)) + lds0 + STAGES * TILE; };
+  auto voff = [&](int db) { return (voff0 ^ (uint32_t)(db << 6)) + lds0 + KST * TILE; };
 
   f32x16 o[DB];
 #pragma unroll
@@ -310,7 +315,7 @@ fwd_kernel(FwdParams p) {
     // both V stages start as zeros, so that the rows past the end of a ragged
     // tile hold zeros or earlier V data, never arbitrary bit patterns
     typedef int i32x4 __attribute__((ext_vector_type(4)));
-    i32x4* z = (i32x4*)(smem + STAGES * TILE);
+    i32x4* z = (i32x4*)(smem + KST * TILE);
 #pragma unroll
     for (int i = tid; i < STAGES * TILE / 16; i += NTHREADS) z[i] = i32x4{};
     // every wave's zeros must land before any wave's first V copy (issued
@@ -334,7 +339,7 @@ fwd_kernel(FwdParams p) {
   if constexpr (VCOL) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      vcol[cc] = lds0 + STAGES * TILE + l32 * 128 + ((((2 * cc + h) ^ (l32 & 7))) << 4);
+      vcol[cc] = lds0 + KST * TILE + l32 * 128 + ((((2 * cc + h) ^ (l32 & 7))) << 4);
   }
   auto read_v = [&](i16x4 (&vr)[2 * DB], uint32_t vstage, auto cc_tag) {
     constexpr int CC = decltype(cc_tag)::value;
@@ -454,7 +459,7 @@ fwd_kernel(FwdParams p) {
 
   // S_t = K_t Q^T with no VALU work to interleave (first tile only)
   auto s_alone = [&](int t, f32x16 (&sn)[NB]) {
-    const char* Ks = smem + (t % STAGES) * TILE;
+    const char* Ks = smem + (t % KST) * TILE;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
     vec8 kr[3][NB], qv[3];
@@ -466,6 +471,17 @@ fwd_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) sn[bb] = Mma<T>::run(kr[kk % 3][bb], qv[kk % 3], sn[bb]);
+    }
+  };
+
+  // KSINGLE: the second barrier of round r, once every wave is past stretch
+  // A (its K reads complete), then this wave's share of the copy of K_{r+1}
+  // into the single K buffer.  Every wave runs it once per round, idle
+  // rounds included, so the barrier counts stay equal.
+  auto mid = [&](int r) {
+    if constexpr (KSINGLE) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (r + 1 < ntile) issue(Kp, r + 1, smem, false);
     }
   };
 
@@ -484,7 +500,7 @@ fwd_kernel(FwdParams p) {
 
     // ---- A: S_{t+1} with the exp2 of chunks 0-1 of S_t
     if (has_next) {
-      const char* Ks = smem + ((t + 1) % STAGES) * TILE;
+      const char* Ks = smem + ((t + 1) % KST) * TILE;
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
       // K (and Q) operands two k-steps ahead of their MFMAs
@@ -508,6 +524,7 @@ fwd_kernel(FwdParams p) {
       exps(sc, 0, 0, 8, rs01, pc);
       exps(sc, 1, 0, 8, rs01, pc);
     }
+    mid(t + 1);
     // chunks 0-1 enter the second GEMM next: their sum check
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs01 <= PMAX)) != 0, 0)) {
       asm volatile("" ::: "memory");
@@ -575,12 +592,13 @@ fwd_kernel(FwdParams p) {
   // the buffers tile r-1 used.  Three stages: wait only for the copies of
   // round r-2 and older (vmcnt counts in order; round r-1's stay in flight),
   // barrier, start K_{r+2} and V_{r+1} into the buffers tile r-2 used.
-  auto kbuf = [&](int t) { return smem + (t % STAGES) * TILE; };
-  auto vbuf = [&](int t) { return smem + (STAGES + t % STAGES) * TILE; };
+  auto kbuf = [&](int t) { return smem + (t % KST) * TILE; };
+  auto vbuf = [&](int t) { return smem + (KST + t % STAGES) * TILE; };
   auto top = [&](int r) {
     if constexpr (STAGES == 2) {
+      // (KSINGLE: K_{r+1} goes out at this round's second barrier instead)
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (r + 1 < ntile) issue(Kp, r + 1, kbuf(r + 1), false);
+      if (!KSINGLE && r + 1 < ntile) issue(Kp, r + 1, kbuf(r + 1), false);
       if (r < ntile) issue(Vp, r, vbuf(r), true);
     } else {
       const int prev = r >= 1 ? (int)(r + 1 < ntile) + (int)(r < ntile) : 0;  // copies of round r-1
@@ -605,6 +623,7 @@ fwd_kernel(FwdParams p) {
   s_alone(0, sA);
   mask(0, sA);
   first_max(sA);
+  mid(0);
   int t = 0;
   for (; t + 2 < n_w; t += 2) {          // unrolled by two: the S sets swap roles
     top(t + 1);
@@ -623,7 +642,10 @@ fwd_kernel(FwdParams p) {
     tile(t, false, sA, sB);
     t += 1;
   }
-  for (int r = t + 1; r <= ntile; ++r) top(r);
+  for (int r = t + 1; r <= ntile; ++r) {
+    top(r);
+    mid(r);
+  }
 
   // ---------------------------------------------------------------- epilogue
   const float l_tot = l_run + wave_half_swap(l_run);
@@ -667,11 +689,14 @@ fwd_kernel(FwdParams p) {
   }
 }
 
-// Dynamic LDS bytes of a forward kernel instance: K and V double buffers, plus
-// the Q block for d = 128.
+// Dynamic LDS bytes of a forward kernel instance: K buffers (one for d = 128
+// with 4 waves, else as many as V's), V stages (three with 8 waves, else two),
+// plus the Q block for d = 128.
 template <int D, int BN, int NW>
 constexpr int fwd_lds_bytes() {
-  return 2 * (NW == 8 ? 3 : 2) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
+  constexpr int vst = NW == 8 ? 3 : 2;
+  constexpr int kst = (D == 128 && NW == 4) ? 1 : vst;
+  return (kst + vst) * BN * D * 2 + (D == 128 ? 32 * NW * D * 2 : 0);
 }
 
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool VARLEN, bool SPLIT = false, bool PACK = false,
