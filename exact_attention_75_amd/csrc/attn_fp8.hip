@@ -279,8 +279,10 @@ hipError_t launch_prepass(const PrepassParams& p, hipStream_t s) {
 // ============================================================================
 //
 // A workgroup of 4 waves owns 128 query rows (one Q scale block), each wave
-// 32 rows; two workgroups share a CU.  Tiles of 64 keys (half a K/V scale
-// block).  Per tile and wave:
+// 32 rows; three workgroups share a CU (three waves per SIMD: the kernel is
+// held to 168 registers, for which the Q block sits in LDS, 48 KiB with the
+// K/V stages, and is read again per tile).  Tiles of 64 keys (half a K/V
+// scale block).  Per tile and wave:
 //   S^T = K Q^T  : 2 blocks of 32 keys x 2 k-steps of 64 channels, on
 //                  v_mfma_scale_f32_32x32x64_f8f6f4 (E8M0 operand scales = 1)
 //   O^T += V^T P^T: one MFMA per 32 output channels, K = the tile's 64 keys.
@@ -333,7 +335,7 @@ __device__ __forceinline__ int swz_v8(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int key_perm8(int r, int b) { return 32 * ((r >> 2) & 1) + 16 * b + 4 * (r >> 3) + (r & 3); }
 
 template <bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int NW = 4, BM = 128, BN = 64, D = 128;
   constexpr int KROW = D;               // bytes per K row
@@ -343,7 +345,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr float NEG_INF = -__builtin_inff();
   constexpr float POFF = 4.0f;          // log2 of P' for a probability of 1 at the running max
   constexpr float PMAX = 448.0f;        // bound on a lane's share of a tile's sum of P' (E4M3 max)
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];   // [K0 | K1 | V0 | V1]
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + BM * D];   // [K0 | K1 | V0 | V1 | Q]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -376,18 +378,26 @@ fwd_fp8_kernel(Fp8FwdParams p) {
   const float lsv_max = log2f(sv_max);
   const int qi = qw + l32;
 
-  // Q fragment: lane holds query qi, channels 64 kk + 32 h .. +31
-  i32x8 qf[2];
+  // Q block in LDS (its 16 registers per lane would cost the third wave per
+  // SIMD): this wave's 32 rows, copied by its own loads (the first tile's
+  // wait covers them), chunk c of row r at c ^ ((r >> 1) & 7) so that the 16
+  // rows one read cycle serves hit 16 different bank groups; rows past the
+  // end read as zeros
   {
-    const int qrow = qi < q_len ? qi : q_len - 1;
-    const uint8_t* qr = Qp + (long long)qrow * qs + 32 * h;
+    uint32_t qdma[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const i32x4 lo = *(const i32x4*)(qr + 64 * kk);
-      const i32x4 hi = *(const i32x4*)(qr + 64 * kk + 16);
-      qf[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int i = 0; i < 4; ++i) {
+      const int pos = i * 64 + lane;
+      const int r = pos >> 3, c = pos & 7;
+      qdma[i] = (uint32_t)(r * qs + ((c ^ ((r >> 1) & 7)) << 4));
     }
+    const uint32_t qbytes = qw < q_len ? (uint32_t)(q_len - qw) * (uint32_t)qs : 0u;
+    copy_rows_to_lds<4>((const void*)(Qp + (long long)(qw < q_len ? qw : 0) * qs), qbytes, smem + 4 * TILE + wave * 4096, qdma);
   }
+  // lane's Q operand of k-step kk: query qi, channels 64 kk + 32 h .. +31
+  int qoff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) qoff[kk] = 4 * TILE + (wave * 32 + l32) * D + (((4 * kk + 2 * h) ^ ((l32 >> 1) & 7)) << 4);
 
   // K / V^T copies (direct to LDS, swizzled through the fetch addresses)
   uint32_t kdma[LOADS], vdma[LOADS];
@@ -422,22 +432,10 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     const int r = 32 * db + l32;
     voff[db] = r * VROW + (((2 * h) ^ swz_v8(r)) << 4);
   }
-  // the second chunk of each 32-byte read: the XOR keeps chunks 2h and 2h+1
-  // adjacent only up to the swizzle, so address it on its own
-  int koff2[2][2], voff2[4];
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int r = key_perm8(l32, bb);
-      koff2[bb][kk] = r * KROW + (((4 * kk + 2 * h + 1) ^ swz_k8(r)) << 4);
-    }
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int r = 32 * db + l32;
-    voff2[db] = r * VROW + (((2 * h + 1) ^ swz_v8(r)) << 4);
-  }
-
+  // The second chunk of each 32-byte read (K, V^T and Q): chunk 2h + 1 sits
+  // at the first one's position XOR 1 (the swizzle acts on the whole chunk
+  // index, and 2h has bit 0 clear), i.e. at byte offset XOR 16; one XOR per
+  // read instead of a second register of offsets.
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
@@ -479,6 +477,13 @@ fwd_fp8_kernel(Fp8FwdParams p) {
     // softmax, and its vector instructions fill the cycles of these MFMAs
     // instead of holding them back (at equal priority the older wave wins
     // the issue arbitration whatever it issues).
+    i32x8 qf[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const i32x4 lo = *(const i32x4*)(smem + qoff[kk]);
+      const i32x4 hi = *(const i32x4*)(smem + (qoff[kk] ^ 16));
+      qf[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     f32x16 s[2];
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -487,7 +492,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const i32x4 lo = *(const i32x4*)(Ks + koff[bb][kk]);
-        const i32x4 hi = *(const i32x4*)(Ks + koff2[bb][kk]);
+        const i32x4 hi = *(const i32x4*)(Ks + (koff[bb][kk] ^ 16));
         s[bb] = mma_fp8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qf[kk], s[bb]);
       }
     }
@@ -556,7 +561,7 @@ fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const i32x4 lo = *(const i32x4*)(Vs + voff[db]);
-      const i32x4 hi = *(const i32x4*)(Vs + voff2[db]);
+      const i32x4 hi = *(const i32x4*)(Vs + (voff[db] ^ 16));
       o[db] = mma_fp8_sa(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db], vscale);
     }
     __builtin_amdgcn_s_setprio(0);
