@@ -19,7 +19,16 @@
 //    (batch x KV head) divides by 8, each XCD is given whole KV groups, so all
 //    query heads that share a KV head, and all query blocks of that head,
 //    stream their K/V through one L2.  Within an XCD the dispatch order is
-//    query block (longest first), then KV group, then query head of the group.
+//    query block (longest first), then KV group, then query head of the group
+//    -- or, group-major, every tile of one KV group (query block longest
+//    first, then query head) before the next group's, so that the XCD's
+//    workgroups read one group's K/V at a time instead of all of its groups'
+//    (c3: 8 MiB of K/V per XCD against a 4 MB L2).  Group-major costs balance
+//    when a group's tiles are few against the XCD's concurrent workgroups: the
+//    last group's longest causal block would start too late.  It is taken for
+//    full attention (equal tiles) and, causal, when a group holds at least
+//    twice as many tiles as the XCD runs at once (its work per slot then
+//    exceeds its longest block).
 #pragma once
 
 #ifdef __HIPCC__
@@ -31,6 +40,7 @@
 namespace attn {
 
 constexpr int kNumXcd = 8;
+constexpr int kCusPerXcd = 32;   // 256 compute units in 8 XCDs
 
 struct TileMap {
   int B, Hq, Hkv, group;  // group = Hq / Hkv
@@ -39,9 +49,12 @@ struct TileMap {
   int ntiles;             // B * Hq * nM
   int xcd;                // 1 when KV groups split evenly over the XCDs
   int gpx;                // KV groups per XCD when xcd == 1
+  int gmaj;               // 1: group-major order within an XCD (needs xcd)
 };
 
-ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m, int causal) {
+// wg_per_cu: workgroups of the kernel that one compute unit holds at once.
+ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m, int causal,
+                                     int wg_per_cu = 1) {
   TileMap t;
   t.B = B;
   t.Hq = Hq;
@@ -53,6 +66,7 @@ ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m
   const int G = B * Hkv;
   t.xcd = (G % kNumXcd == 0) ? 1 : 0;
   t.gpx = t.xcd ? G / kNumXcd : 0;
+  t.gmaj = (t.xcd && (!causal || t.nM * t.group >= 2 * kCusPerXcd * wg_per_cu)) ? 1 : 0;
   return t;
 }
 
@@ -60,7 +74,15 @@ ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m
 // A bijection for every TileMap.
 ATTN_HD inline void tile_decode(const TileMap& t, int p, int& b, int& hq, int& m) {
   int m_rev, g, hg;
-  if (t.xcd) {
+  if (t.xcd && t.gmaj) {
+    const int x = p % kNumXcd, slot = p / kNumXcd;
+    const int per_g = t.nM * t.group;     // tiles of one KV group
+    const int gl = slot / per_g;
+    const int r = slot - gl * per_g;
+    g = x * t.gpx + gl;
+    m_rev = r / t.group;
+    hg = r % t.group;
+  } else if (t.xcd) {
     const int x = p % kNumXcd, slot = p / kNumXcd;
     const int per_row = t.gpx * t.group;  // tiles of one query-block row in one XCD
     m_rev = slot / per_row;
