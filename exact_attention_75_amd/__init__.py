@@ -59,7 +59,7 @@ def library() -> ctypes.CDLL:
     L.attn_default_signs.argtypes = [ctypes.POINTER(ctypes.c_float), I]
     L.attn_default_signs.restype = I
     IP = ctypes.POINTER(ctypes.c_int)
-    L.attn_tile_of.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
+    L.attn_tile_of.argtypes = [I, I, I, I, I, I, I, IP, IP, IP]
     L.attn_tile_of.restype = I
     L.attn_grid_size.argtypes = [I, I, I, I, I, IP, IP]
     L.attn_grid_size.restype = I
@@ -367,9 +367,9 @@ def default_signs(n: int = 128):
     return [float(x) for x in buf]
 
 
-def tile_of(p: int, B: int, Hq: int, Hkv: int, Sq: int, block_m: int, causal: bool, wg_per_cu: int = 1):
+def tile_of(p: int, B: int, Hq: int, Hkv: int, Sq: int, block_m: int, causal: bool):
     b, h, m = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    rc = library().attn_tile_of(p, B, Hq, Hkv, Sq, block_m, int(causal), wg_per_cu, ctypes.byref(b),
+    rc = library().attn_tile_of(p, B, Hq, Hkv, Sq, block_m, int(causal), ctypes.byref(b),
                                 ctypes.byref(h), ctypes.byref(m))
     _check(rc, "attn_tile_of")
     return b.value, h.value, m.value

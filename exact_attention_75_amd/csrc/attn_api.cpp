@@ -230,10 +230,7 @@ int fwd16_dense(const void* q, const void* k, const void* v, void* o, float* lse
   p.pack = pack;
   const int g = Hq / Hkv;
   const int bm = (pack || splits > 1) ? kSplitBlockM : attn::fwd_block_m(dtype, d, 0);
-  // 256-row tiles: one workgroup per CU; 128-row (4-wave) tiles: two
-  const int wpc = bm == 256 ? 1 : 2;
-  p.tm = pack ? attn::make_tile_map(B, Hkv, Hkv, Sq * g, bm, causal, wpc)
-              : attn::make_tile_map(B, Hq, Hkv, Sq, bm, causal, wpc);
+  p.tm = pack ? attn::make_tile_map(B, Hkv, Hkv, Sq * g, bm, causal) : attn::make_tile_map(B, Hq, Hkv, Sq, bm, causal);
   if (splits <= 1) {
     p.grid = p.tm.ntiles;
     hipError_t e = launch_gate();
@@ -296,11 +293,11 @@ int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* 
   return ATTN_OK;
 }
 
-int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal, int wg_per_cu, int* b_out,
+int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal, int* b_out,
                  int* h_out, int* m_out) {
   if (!b_out || !h_out || !m_out) return ATTN_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || block_m <= 0 || Hq % Hkv || wg_per_cu <= 0) return ATTN_ERR_SHAPE;
-  attn::TileMap tm = attn::make_tile_map(B, Hq, Hkv, Sq, block_m, causal, wg_per_cu);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || block_m <= 0 || Hq % Hkv) return ATTN_ERR_SHAPE;
+  attn::TileMap tm = attn::make_tile_map(B, Hq, Hkv, Sq, block_m, causal);
   if (p < 0 || p >= tm.ntiles) return ATTN_ERR_SHAPE;
   attn::tile_decode(tm, p, *b_out, *h_out, *m_out);
   return ATTN_OK;
@@ -330,7 +327,7 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   p.Sk = Sk;
   p.group = Hq / Hkv;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_fp8_block_m(), causal, attn::kFp8WgPerCu);
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, attn::fwd_fp8_block_m(), causal);
   p.grid = p.tm.ntiles;
   hipError_t e = launch_gate();
   if (e == hipSuccess) e = attn::launch_fwd_fp8(p, causal, (hipStream_t)stream);
@@ -562,7 +559,7 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* ls
     p.softcap_a = softcap / scale;
     p.softcap_b2 = 2.f * scale * 1.4426950408889634f / softcap;
   }
-  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal, 2);
+  p.tm = attn::make_tile_map(B, Hq, Hkv, Sq, kSplitBlockM, causal);
   p.grid = p.tm.ntiles;
   hipError_t e = launch_gate();
   if (e == hipSuccess) e = attn::launch_fwd(p, dtype, d, causal, 0, (hipStream_t)stream);

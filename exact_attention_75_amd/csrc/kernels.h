@@ -132,8 +132,6 @@ constexpr float default_sign(int i) {
 int fwd_block_m(int dtype, int d, int varlen);
 // Query rows per workgroup of the fp8 forward.
 int fwd_fp8_block_m();
-// workgroups of the fp8 kernel one compute unit holds (three waves per SIMD)
-constexpr int kFp8WgPerCu = 3;
 
 // Returns hipSuccess or the launch error.  p.pack selects the PackGQA
 // variant (128-row blocks) for dense inputs.

@@ -19,16 +19,14 @@
 //    (batch x KV head) divides by 8, each XCD is given whole KV groups, so all
 //    query heads that share a KV head, and all query blocks of that head,
 //    stream their K/V through one L2.  Within an XCD the dispatch order is
-//    query block (longest first), then KV group, then query head of the group
-//    -- or, group-major, every tile of one KV group (query block longest
-//    first, then query head) before the next group's, so that the XCD's
-//    workgroups read one group's K/V at a time instead of all of its groups'
-//    (c3: 8 MiB of K/V per XCD against a 4 MB L2).  Group-major costs balance
-//    when a group's tiles are few against the XCD's concurrent workgroups: the
-//    last group's longest causal block would start too late.  It is taken for
-//    full attention (equal tiles) and, causal, when a group holds at least
-//    twice as many tiles as the XCD runs at once (its work per slot then
-//    exceeds its longest block).
+//    query block (longest first), then KV group, then query head of the group.
+//    Full attention (tiles of equal work) instead runs group-major: every
+//    tile of one KV group before the next group's, so the XCD's workgroups
+//    read one group's K/V at a time instead of all of its groups' (c5: 2
+//    groups of 4 MiB per XCD against a 4 MB L2; HBM reads 5.4x -> 2.7x the
+//    algorithmic bytes, 1.3 % faster).  Causal launches keep the query-block
+//    order: there the longest-first balance is worth more than the L2
+//    (group-major measured 0.3-0.6 % slower on the 8K causal shapes).
 #pragma once
 
 #ifdef __HIPCC__
@@ -40,7 +38,6 @@
 namespace attn {
 
 constexpr int kNumXcd = 8;
-constexpr int kCusPerXcd = 32;   // 256 compute units in 8 XCDs
 
 struct TileMap {
   int B, Hq, Hkv, group;  // group = Hq / Hkv
@@ -52,9 +49,7 @@ struct TileMap {
   int gmaj;               // 1: group-major order within an XCD (needs xcd)
 };
 
-// wg_per_cu: workgroups of the kernel that one compute unit holds at once.
-ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m, int causal,
-                                     int wg_per_cu = 1) {
+ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m, int causal) {
   TileMap t;
   t.B = B;
   t.Hq = Hq;
@@ -66,7 +61,7 @@ ATTN_HD inline TileMap make_tile_map(int B, int Hq, int Hkv, int Sq, int block_m
   const int G = B * Hkv;
   t.xcd = (G % kNumXcd == 0) ? 1 : 0;
   t.gpx = t.xcd ? G / kNumXcd : 0;
-  t.gmaj = (t.xcd && (!causal || t.nM * t.group >= 2 * kCusPerXcd * wg_per_cu)) ? 1 : 0;
+  t.gmaj = (t.xcd && !causal) ? 1 : 0;
   return t;
 }
 

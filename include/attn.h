@@ -335,14 +335,11 @@ int attn_default_signs(float* signs_host, int n);
 /* Tile order of the forward kernel's scheduler, evaluated on the host (for
  * inspection and tests): for workgroup index p of a dense launch, writes the
  * (batch, query head, query block) it processes.  block_m is the number of
- * query rows per tile, wg_per_cu the number of the kernel's workgroups one
- * compute unit holds at once (1 for 256-row tiles and the head-packed
- * layout, 2 for 128-row tiles, 3 for the fp8 kernel; it decides whether an
- * XCD takes its KV groups one after another).  (The head-packed layout of
- * dense d = 128 inputs with a group Hq / Hkv that is a multiple of 4 is this
- * order for Hq / 4 "heads" and block_m = 64: entry h stands for query heads
- * 4 h .. 4 h + 3.)  Returns ATTN_OK or ATTN_ERR_SHAPE / ATTN_ERR_NULL. */
-int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal, int wg_per_cu,
+ * query rows per tile.  (The head-packed layout of dense d = 128 inputs with a
+ * group Hq / Hkv that is a multiple of 4 is this order for Hq / 4 "heads" and
+ * block_m = 64: entry h stands for query heads 4 h .. 4 h + 3.)  Returns
+ * ATTN_OK or ATTN_ERR_SHAPE / ATTN_ERR_NULL. */
+int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal,
                  int* b_out, int* h_out, int* m_out);
 
 /* Number of workgroups a dense launch uses, and query rows per tile, for

@@ -99,24 +99,23 @@ def test_default_signs_match_generator(lib):
     assert ea.default_signs(128) == W.hadamard_signs(128, 55).tolist()
 
 
-def tiles(B, Hq, Hkv, Sq, causal, bm=128, wpc=1):
+def tiles(B, Hq, Hkv, Sq, causal, bm=128):
     nM = (Sq + bm - 1) // bm
-    return [ea.tile_of(p, B, Hq, Hkv, Sq, bm, causal, wpc) for p in range(B * Hq * nM)], nM
+    return [ea.tile_of(p, B, Hq, Hkv, Sq, bm, causal) for p in range(B * Hq * nM)], nM
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 2, 256), (4, 16, 16, 2048), (2, 32, 8, 1024), (3, 6, 2, 300),
                                    (1, 8, 1, 129), (2, 32, 8, 8192), (1, 16, 16, 16384)])
 @pytest.mark.parametrize("causal", [0, 1])
-@pytest.mark.parametrize("wpc", [1, 3])
-def test_tile_map_is_bijection(lib, shape, causal, wpc):
+def test_tile_map_is_bijection(lib, shape, causal):
     B, Hq, Hkv, Sq = shape
-    ts, nM = tiles(B, Hq, Hkv, Sq, causal, wpc=wpc)
+    ts, nM = tiles(B, Hq, Hkv, Sq, causal)
     assert sorted(ts) == sorted((b, h, m) for b in range(B) for h in range(Hq) for m in range(nM))
 
 
 def xcd_runs(ts, group):
-    """Per XCD (workgroups p = x mod 8): the query blocks in dispatch order
-    and the KV groups in order of first appearance."""
+    """Per XCD (workgroups p = x mod 8): its workgroups in dispatch order and
+    its KV groups in order of first appearance."""
     out = []
     for x in range(8):
         mine = ts[x::8]
@@ -129,11 +128,10 @@ def xcd_runs(ts, group):
 
 
 def test_tile_map_lpt_and_xcd_affinity(lib):
-    # 16 KV groups: 2 per XCD; 64 tiles per group, below 2 x 32 CUs x 2
-    # workgroups: query block major, longest first
+    # causal, 16 KV groups: 2 per XCD, query blocks longest first
     B, Hq, Hkv, Sq = 2, 32, 8, 2048
     group = Hq // Hkv
-    ts, nM = tiles(B, Hq, Hkv, Sq, 1, wpc=2)
+    ts, nM = tiles(B, Hq, Hkv, Sq, 1)
     for mine, kv in xcd_runs(ts, group):
         ms = [m for _, _, m in mine]
         assert ms == sorted(ms, reverse=True)          # longest (latest) query blocks first
@@ -144,37 +142,21 @@ def test_tile_map_lpt_and_xcd_affinity(lib):
     assert ms == sorted(ms, reverse=True)
 
 
-@pytest.mark.parametrize("causal,wpc", [(1, 1), (0, 2), (0, 3)])
-def test_tile_map_group_major(lib, causal, wpc):
-    # 64 tiles per KV group: enough for one workgroup per CU (2 x 32), and
-    # any full attention: every XCD finishes one KV group before the next,
-    # longest query block first within it
-    B, Hq, Hkv, Sq = 2, 32, 8, 2048
+@pytest.mark.parametrize("shape", [(2, 32, 8, 2048), (1, 16, 16, 16384)])
+def test_tile_map_group_major_for_full_attention(lib, shape):
+    # full attention: every XCD finishes one KV group (all its query blocks
+    # and heads) before the next
+    B, Hq, Hkv, Sq = shape
     group = Hq // Hkv
-    ts, nM = tiles(B, Hq, Hkv, Sq, causal, wpc=wpc)
+    ts, nM = tiles(B, Hq, Hkv, Sq, 0)
     for mine, kv in xcd_runs(ts, group):
-        assert len(kv) == 2
+        assert len(kv) == B * Hkv // 8
         per = nM * group
         for i, g in enumerate(kv):
             run = mine[i * per:(i + 1) * per]
             assert {(b, h // group) for b, h, _ in run} == {g}
             ms = [m for _, _, m in run]
-            assert ms == sorted(ms, reverse=bool(causal))
-
-
-def test_tile_map_workload_orders(lib):
-    # c3 head-packed (8 "heads" of 64 rows, 2 groups per XCD, 128 tiles per
-    # group, one workgroup per CU): group-major; c2 (64 KV groups, 8 tiles
-    # each): query block major; c3fp8 (128-row tiles, group 4, three
-    # workgroups per CU: 256 >= 192): group-major
-    def first_groups(ts, group, n):
-        return [len({(b, h // group) for b, h, _ in ts[x::8][:n]}) for x in range(8)]
-    ts, _ = tiles(2, 8, 8, 8192, 1, bm=64, wpc=1)
-    assert first_groups(ts, 1, 32) == [1] * 8
-    ts, _ = tiles(4, 16, 16, 2048, 1, bm=256, wpc=1)
-    assert first_groups(ts, 1, 32) == [8] * 8
-    ts, _ = tiles(2, 32, 8, 8192, 1, bm=128, wpc=3)
-    assert first_groups(ts, 4, 96) == [1] * 8
+            assert ms == sorted(ms)
 
 
 def test_tile_of_rejects_bad_args(lib):
@@ -182,8 +164,6 @@ def test_tile_of_rejects_bad_args(lib):
         ea.tile_of(10**6, 1, 2, 2, 256, 128, False)
     with pytest.raises(ea.AttnError):
         ea.tile_of(0, 1, 3, 2, 256, 128, False)
-    with pytest.raises(ea.AttnError):
-        ea.tile_of(0, 1, 2, 2, 256, 128, False, 0)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,n", [
