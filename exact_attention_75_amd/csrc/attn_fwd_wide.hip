@@ -32,9 +32,20 @@
 //    no per-tile row max is needed (P <= PMAX, far inside the fp32, bf16 and
 //    fp16 ranges).  Then -- rarely -- the tile's row max is taken, O and l
 //    are rescaled and the tile's probabilities recomputed.
+//  * Head-packed launches with more tiles than compute units are
+//    persistent: one workgroup per CU runs a balanced share of its XCD's
+//    longest-first tile list.  Between two tiles the next tile's Q rows are
+//    loaded during the last P V of the current one (its Q registers are
+//    free by then), and the finished tile's epilogue (O / l, LSE, stores)
+//    runs after the next tile's first S, which leaves O alone, so its vector
+//    work sits beside those MFMAs.  A fresh workgroup per tile instead
+//    waits for its Q and first K/V tiles and runs its epilogue alone, ~9 us
+//    of fixed cost per tile (measured on full attention at 8K and 16K).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include <type_traits>
 
@@ -100,39 +111,59 @@ fwd_wide_kernel(FwdParams p) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  int b, hq, mblk;
-  tile_decode(p.tm, blockIdx.x, b, hq, mblk);
-  if constexpr (H4) hq = 4 * hq + wave;
   const int q_len = p.Sq, kv_len = p.Sk;
-  const int hkv = hq / p.group;
-  const T* Qp = (const T*)p.q + (long long)b * p.q_batch_stride + hq * D;
-  const T* Kp = (const T*)p.k + (long long)b * p.kv_batch_stride + hkv * D;
-  const T* Vp = (const T*)p.v + (long long)b * p.kv_batch_stride + hkv * D;
-  T* Op = (T*)p.o + (long long)b * p.q_batch_stride + hq * D;
-  const long long lse_off = ((long long)b * p.Hq + hq) * p.Sq;
   const int qs = p.q_tok_stride;
   const int ks = p.kv_tok_stride;
-
   constexpr int ROWS = H4 ? 64 : BM;                    // query rows per head of the workgroup
-  const int q0 = mblk * ROWS;
-  const int qw = H4 ? q0 : q0 + 64 * wave;              // first query row of this wave
-  const int q_hi = q0 + ROWS < q_len ? q0 + ROWS : q_len;
-  const int kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
-  const int ntile = (kv_end + BN - 1) / BN;
-  // key tiles this wave computes: up to its diagonal when causal, none when
-  // all its rows are past the end of the sequence
-  int n_w = CAUSAL ? min(ntile, (qw + 63) / BN + 1) : ntile;
-  if (qw >= q_len) n_w = 0;
+
+  // ---------------------------------------------------------------- tiles
+  // A workgroup runs one tile, or (persistent launch: fewer workgroups than
+  // tiles) the tiles j, 2 J - 1 - j, 2 J + j, ... of its XCD's longest-first
+  // list, j its index among the XCD's J workgroups.
+  const int ntl = p.tm.ntiles;
+  const bool persist = H4 && (int)gridDim.x < ntl;
+  const int xg = blockIdx.x % kNumXcd, jg = blockIdx.x / kNumXcd, JG = gridDim.x / kNumXcd;
+  auto tile_of_round = [&](int rr) {
+    if (!persist) return rr == 0 ? (int)blockIdx.x : ntl;
+    const int sl = rr * JG + ((rr & 1) ? JG - 1 - jg : jg);
+    return xg + kNumXcd * sl;
+  };
+  int b, hq, mblk, hkv, q0, qw, q_hi, kv_end, ntile, n_w, t_edge;
+  const T *Qp, *Kp, *Vp;
+  T* Op;
+  long long lse_off;
+  auto tile_setup = [&](int pt) {
+    tile_decode(p.tm, pt, b, hq, mblk);
+    if constexpr (H4) hq = 4 * hq + wave;
+    hkv = hq / p.group;
+    Qp = (const T*)p.q + (long long)b * p.q_batch_stride + hq * D;
+    Kp = (const T*)p.k + (long long)b * p.kv_batch_stride + hkv * D;
+    Vp = (const T*)p.v + (long long)b * p.kv_batch_stride + hkv * D;
+    Op = (T*)p.o + (long long)b * p.q_batch_stride + hq * D;
+    lse_off = ((long long)b * p.Hq + hq) * p.Sq;
+    q0 = mblk * ROWS;
+    qw = H4 ? q0 : q0 + 64 * wave;              // first query row of this wave
+    q_hi = q0 + ROWS < q_len ? q0 + ROWS : q_len;
+    kv_end = CAUSAL ? (kv_len < q_hi ? kv_len : q_hi) : kv_len;
+    ntile = (kv_end + BN - 1) / BN;
+    // key tiles this wave computes: up to its diagonal when causal, none when
+    // all its rows are past the end of the sequence
+    n_w = CAUSAL ? min(ntile, (qw + 63) / BN + 1) : ntile;
+    if (qw >= q_len) n_w = 0;
+    // Tile t needs the mask when it reaches past the last key (t BN + BN >
+    // kv_len) or, causal, past the wave's first row (t BN + BN - 1 > qw); both
+    // hold from some t on, so one comparison with the first such t decides.
+    t_edge = CAUSAL ? min(kv_len / BN, (qw + 1) / BN) : kv_len / BN;
+  };
 
   // ---------------------------------------------------------------- Q, O
   // B operand of S^T = K Q^T: lane holds query qw + 32 qb + l32, head-dim
   // 16 kk + 8 h .. +7 (rows past the end repeat the last row; never stored).
   // The loads land before the first round's barrier (vmcnt(0)).
-  o_zero();
-  {
+  auto q_issue_at = [&](const T* qbase, int qwv) {
     auto qrow = [&](int qb) {
-      const int r = qw + 32 * qb + l32;
-      return Qp + (long long)(r < q_len ? r : q_len - 1) * qs + 8 * h;
+      const int r = qwv + 32 * qb + l32;
+      return qbase + (long long)(r < q_len ? r : q_len - 1) * qs + 8 * h;
     };
     const T* q0p = qrow(0);
     const T* q1p = qrow(1);
@@ -140,7 +171,19 @@ fwd_wide_kernel(FwdParams p) {
     q_load<0, 4>(q0p + 64);  q_load<0, 5>(q0p + 80);  q_load<0, 6>(q0p + 96);  q_load<0, 7>(q0p + 112);
     q_load<1, 0>(q1p + 0);   q_load<1, 1>(q1p + 16);  q_load<1, 2>(q1p + 32);  q_load<1, 3>(q1p + 48);
     q_load<1, 4>(q1p + 64);  q_load<1, 5>(q1p + 80);  q_load<1, 6>(q1p + 96);  q_load<1, 7>(q1p + 112);
-  }
+  };
+  // the Q rows of tile pt, without touching the current tile's state
+  // (QLOADS load instructions per wave)
+  constexpr int QLOADS = 2 * KT;
+  auto q_issue_tile = [&](int ptv) {
+    int bv, hv, mv;
+    tile_decode(p.tm, ptv, bv, hv, mv);
+    if constexpr (H4) hv = 4 * hv + wave;
+    const int q0v = mv * ROWS;
+    q_issue_at((const T*)p.q + (long long)bv * p.q_batch_stride + hv * D, H4 ? q0v : q0v + 64 * wave);
+  };
+  int next_pt = ntl;     // the workgroup's next tile (ntl: none)
+  bool q_early = false;  // its Q loads went out during this tile's last iteration
 
   // ---------------------------------------------------------------- K/V copies
   // Lane L of copy i fetches the global 16-byte chunk that belongs at LDS
@@ -163,7 +206,7 @@ fwd_wide_kernel(FwdParams p) {
   }
   static_assert(!VCOL || BN * 2 == 8 * 16, "V^T tile rows of 8 chunks");
   // column-major V: this (batch, KV head)'s [D, Sk] plane
-  const T* Vt = VCOL ? (const T*)p.v + ((long long)b * p.Hkv + hkv) * D * p.Sk : nullptr;
+  const T* Vt = nullptr;
   // the copies of one K or V tile: source, size and destination, all
   // wave-uniform
   struct Copy {
@@ -188,9 +231,13 @@ fwd_wide_kernel(FwdParams p) {
     int keys;
     int slot;
   };
-  Stream ks_k{(uint64_t)(uintptr_t)Kp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
-  Stream ks_v = VCOL ? Stream{(uint64_t)(uintptr_t)Vt, (uint32_t)(D * p.Sk) * 2u, (uint32_t)(BN * 2), kv_end, 0}
-                     : Stream{(uint64_t)(uintptr_t)Vp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
+  Stream ks_k, ks_v;
+  auto streams_setup = [&]() {
+    if constexpr (VCOL) Vt = (const T*)p.v + ((long long)b * p.Hkv + hkv) * D * p.Sk;
+    ks_k = Stream{(uint64_t)(uintptr_t)Kp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
+    ks_v = VCOL ? Stream{(uint64_t)(uintptr_t)Vt, (uint32_t)(D * p.Sk) * 2u, (uint32_t)(BN * 2), kv_end, 0}
+                : Stream{(uint64_t)(uintptr_t)Vp, (uint32_t)kv_end * (uint32_t)ks * 2u, (uint32_t)(BN * ks * 2), kv_end, 0};
+  };
   auto next_copy = [&](Stream& st, int ring) {
     const Copy cp{(const void*)(uintptr_t)st.src, st.keys > 0 ? st.bytes : 0u,
                   smem + (ring + st.slot) * TILE + wave * LOADS * 1024};
@@ -272,19 +319,17 @@ fwd_wide_kernel(FwdParams p) {
   // of the running sum over the fp32 probabilities, and the exponent offset
   // of the current tile
   float m_run[QB], l_run[QB], msub[QB];
+  auto softmax_init = [&]() {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = NEG_INF;
-    l_run[qb] = 0.f;
-    msub[qb] = 0.f;
-  }
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = NEG_INF;
+      l_run[qb] = 0.f;
+      msub[qb] = 0.f;
+    }
+  };
 
   // mask: element i of s[qb][bb] is key j0 + 32 bb + 16 (i/8) + 8 h + i%8 for
   // query qw + 32 qb + l32
-  // Tile t needs the mask when it reaches past the last key (t BN + BN >
-  // kv_len) or, causal, past the wave's first row (t BN + BN - 1 > qw); both
-  // hold from some t on, so one comparison with the first such t decides.
-  const int t_edge = CAUSAL ? min(kv_len / BN, (qw + 1) / BN) : kv_len / BN;
   auto mask = [&](int t, f32x16(&sn)[QB][NB]) {
     const int j0 = t * BN;
     if (t >= t_edge) {
@@ -439,6 +484,14 @@ fwd_wide_kernel(FwdParams p) {
       vc = next_copy(ks_v, STAGES);    // V_{t+VLA}
     } else {
       top(t);
+      // this tile's last S is done: the Q registers can take the next tile's
+      // rows, which then arrive behind this last P V and the epilogue
+      if constexpr (H4) {
+        if (next_pt < ntl) {
+          q_issue_tile(next_pt);
+          q_early = true;
+        }
+      }
     }
     const uint32_t kst = (uint32_t)(slot_of(t) * TILE);       // K_t
     const uint32_t vst = (uint32_t)(slot_of(t - 1) * TILE);   // V_{t-1}
@@ -600,48 +653,40 @@ fwd_wide_kernel(FwdParams p) {
   // prologue rounds -KLA .. -1: K_0 .. K_{KLA-1} and V_{VLA-KLA} .. V_{VLA-1}
   // (a V tile before the first is an empty copy, so that every round issues
   // the same number of copies)
+  auto prologue = [&]() {
 #pragma unroll
-  for (int r = -KLA; r < 0; ++r) {
-    issue_copy(next_copy(ks_k, 0), kdma);
-    if (r + VLA >= 0) issue_copy(next_copy(ks_v, STAGES), vdma);
-    else issue_copy(Copy{Kp, 0u, smem + (STAGES + slot_of(r + VLA)) * TILE + wave * LOADS * 1024}, vdma);
-  }
-  f32x16 s0[QB][NB], s1[QB][NB];
-  vec8 p0[QB][NC], p1[QB][NC];
-  typedef std::true_type Y;
-  typedef std::false_type N;
-  int t = 0;
-  if (n_w > 0) {
-    iter(0, Y{}, N{}, s0, s1, p0, p1);
-    t = 1;
-    for (; t + 2 <= n_w; t += 2) {
-      iter(t, Y{}, Y{}, s1, s0, p1, p0);
-      iter(t + 1, Y{}, Y{}, s0, s1, p0, p1);
+    for (int r = -KLA; r < 0; ++r) {
+      issue_copy(next_copy(ks_k, 0), kdma);
+      if (r + VLA >= 0) issue_copy(next_copy(ks_v, STAGES), vdma);
+      else issue_copy(Copy{Kp, 0u, smem + (STAGES + slot_of(r + VLA)) * TILE + wave * LOADS * 1024}, vdma);
     }
-    // t is odd, t >= n_w - 1
-    if (t < n_w) {
-      iter(t, Y{}, Y{}, s1, s0, p1, p0);
-      iter(t + 1, N{}, Y{}, s0, s1, p0, p1);
-      t += 2;
-    } else {
-      iter(t, N{}, Y{}, s1, s0, p1, p0);
-      t += 1;
-    }
-  }
-  // idle rounds keep the barrier count equal across the waves
-  for (; t <= ntile; ++t) top(t);
-  // no copy may still be writing LDS when the workgroup ends
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  acc_read_pad();
+  };
 
   // ---------------------------------------------------------------- epilogue
+  // O / l and the LSE of a finished tile.  With several tiles per workgroup
+  // it runs after the next tile's first S (which leaves O alone), so its
+  // vector work sits beside those MFMAs; what it needs of the finished tile
+  // is kept in the e_ values.
+  float e_inv[QB], e_lse[QB];
+  int e_qw = 0;
+  T* e_op = nullptr;
+  long long e_lse_off = 0;
+  auto epi_save = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = l_run[qb] + wave_half_swap(l_run[qb]);
+      e_inv[qb] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      e_lse[qb] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
+    }
+    e_qw = qw;
+    e_op = Op;
+    e_lse_off = lse_off;
+  };
   auto store = [&](auto qb_tag, const f32x16 (&ob)[DB]) {
     constexpr int QBI = decltype(qb_tag)::value;
-    const float l_tot = l_run[QBI] + wave_half_swap(l_run[QBI]);
-    const int qi = qw + 32 * QBI + l32;
+    const int qi = e_qw + 32 * QBI + l32;
     if (qi < q_len) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      T* orow = Op + (long long)qi * qs;
+      T* orow = e_op + (long long)qi * qs;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -649,23 +694,104 @@ fwd_wide_kernel(FwdParams p) {
           typedef T T4 __attribute__((ext_vector_type(4)));
           T4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (T)(ob[db][4 * g + e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = (T)(ob[db][4 * g + e] * e_inv[QBI]);
           *(T4*)(orow + 32 * db + 8 * g + 4 * h) = w;
         }
-      if (p.lse != nullptr && h == 0) {
-        const float lse = l_tot > 0.f ? (m_run[QBI] + log2f(l_tot)) * 0.69314718055994530942f : NEG_INF;
-        p.lse[lse_off + qi] = lse;
-      }
+      if (p.lse != nullptr && h == 0) p.lse[e_lse_off + qi] = e_lse[QBI];
     }
   };
-  {
-    const f32x16 ob[DB] = {acc_read<0, 0>(), acc_read<0, 1>(), acc_read<0, 2>(), acc_read<0, 3>()};
-    store(ic<0>{}, ob);
+  auto epi_store = [&]() {
+    acc_read_pad();
+    {
+      const f32x16 ob[DB] = {acc_read<0, 0>(), acc_read<0, 1>(), acc_read<0, 2>(), acc_read<0, 3>()};
+      store(ic<0>{}, ob);
+    }
+    {
+      const f32x16 ob[DB] = {acc_read<1, 0>(), acc_read<1, 1>(), acc_read<1, 2>(), acc_read<1, 3>()};
+      store(ic<1>{}, ob);
+    }
+  };
+
+  // ---------------------------------------------------------------- tiles
+  f32x16 s0[QB][NB], s1[QB][NB];
+  vec8 p0[QB][NC], p1[QB][NC];
+  typedef std::true_type Y;
+  typedef std::false_type N;
+  int rr = 0;
+  int pt = tile_of_round(0);
+  if (pt >= ntl) return;
+  tile_setup(pt);
+  streams_setup();
+  o_zero();
+  q_issue_at(Qp, qw);
+  prologue();
+  bool pending = false;   // a finished tile's O still waits in the accumulators
+  for (;;) {
+    softmax_init();
+    next_pt = tile_of_round(rr + 1);
+    int t = 0;
+    if (n_w > 0) {
+      iter(0, Y{}, N{}, s0, s1, p0, p1);
+      if (pending) {
+        epi_store();
+        o_zero();
+        pending = false;
+      }
+      t = 1;
+      for (; t + 2 <= n_w; t += 2) {
+        iter(t, Y{}, Y{}, s1, s0, p1, p0);
+        iter(t + 1, Y{}, Y{}, s0, s1, p0, p1);
+      }
+      // t is odd, t >= n_w - 1
+      if (t < n_w) {
+        iter(t, Y{}, Y{}, s1, s0, p1, p0);
+        iter(t + 1, N{}, Y{}, s0, s1, p0, p1);
+        t += 2;
+      } else {
+        iter(t, N{}, Y{}, s1, s0, p1, p0);
+        t += 1;
+      }
+    }
+    if (pending) {
+      epi_store();
+      o_zero();
+      pending = false;
+    }
+    // idle rounds keep the barrier count equal across the waves
+    const bool idle = t <= ntile;
+    for (; t <= ntile; ++t) top(t);
+    // no copy may still be writing LDS past this point; the next tile's Q
+    // loads, issued after the last copies, may stay in flight
+    if (q_early && !idle) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QLOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    epi_save();
+    pending = true;
+    pt = tile_of_round(++rr);
+    if (pt >= ntl) break;
+    // every wave is past its last LDS read of this tile before the next
+    // tile's copies go out; the Q registers are free (its last S is done)
+    asm volatile("s_barrier" ::: "memory");
+    tile_setup(pt);
+    streams_setup();
+    if (!q_early) q_issue_at(Qp, qw);
+    q_early = false;
+    prologue();
   }
-  {
-    const f32x16 ob[DB] = {acc_read<1, 0>(), acc_read<1, 1>(), acc_read<1, 2>(), acc_read<1, 3>()};
-    store(ic<1>{}, ob);
+  epi_store();
+}
+
+// Compute units of the current device (read once per device).
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
+  return n > 0 ? n : 0;
 }
 
 template <typename T, bool CAUSAL, bool H4, bool VCOL>
@@ -688,7 +814,10 @@ static hipError_t launch_wide_t(const FwdParams& p, int causal, hipStream_t s) {
     // four query heads of one KV head per workgroup, 64 rows each
     FwdParams q = p;
     q.tm = make_tile_map(p.B, p.Hq / 4, p.Hkv, p.Sq, 64, causal);
-    q.grid = q.tm.ntiles;
+    // persistent when there are more tiles than CUs: one workgroup per CU,
+    // the same number on every XCD
+    const int cus = device_cus() / kNumXcd * kNumXcd;
+    q.grid = (cus > 0 && q.tm.ntiles > cus) ? cus : q.tm.ntiles;
     return causal ? launch_wide_one<T, true, true, VCOL>(q, s) : launch_wide_one<T, false, true, VCOL>(q, s);
   }
   return causal ? launch_wide_one<T, true, false, VCOL>(p, s) : launch_wide_one<T, false, false, VCOL>(p, s);

@@ -281,6 +281,25 @@ def test_c2_full_heads(ea):
                 l_ref[b:b + 1, h:h + 1], f"c2 b{b} h{h} full")
 
 
+@pytest.mark.parametrize("shape,causal", [
+    ((1, 2560, 32, 8), True),    # 8 KV groups x 40 blocks = 320 tiles, XCD affinity
+    ((1, 2560, 32, 8), False),   # the same, full attention (groups one after another)
+    ((3, 3200, 8, 2), True),     # 6 KV groups (no even XCD split) x 50 blocks = 300 tiles
+])
+def test_persistent_head_packed(ea, shape, causal):
+    # d = 128 with groups of four query heads runs the head-packed wide
+    # kernel; with more 64-row tiles than compute units each workgroup runs
+    # several tiles in turn (the next tile's Q loaded during the last P V,
+    # the finished tile's epilogue after the next tile's first S): every
+    # output element against the oracle
+    B, S, Hq, Hkv = shape
+    print(f"[case] persistent head-packed B={B} S={S} Hq={Hq} Hkv={Hkv} causal={causal}", flush=True)
+    q, k, v = W.make_dense(B, S, S, Hq, Hkv, 128, "bf16", seed=31 + B)
+    o, lse = run_dense(ea, q, k, v, causal)
+    o_ref, l_ref = A.attention(q, k, v, 1 / math.sqrt(128), causal)
+    compare(o, lse, o_ref, l_ref, f"persistent B{B} S{S} Hq{Hq} Hkv{Hkv} c{int(causal)}")
+
+
 def test_c4_varlen(ea):
     w = W.CONFIGS["c4"]
     inp = W.make_inputs(w)
