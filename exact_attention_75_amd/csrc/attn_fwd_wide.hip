@@ -37,8 +37,9 @@
 //    longest-first tile list.  Between two tiles the next tile's Q rows are
 //    loaded during the last P V of the current one (its Q registers are
 //    free by then), and the finished tile's epilogue (O / l, LSE, stores)
-//    runs after the next tile's first S, which leaves O alone, so its vector
-//    work sits beside those MFMAs.  A fresh workgroup per tile instead
+//    runs after the next tile's first iteration (its S and row max leave O
+//    alone), with that tile's copies already in flight; its stores drain
+//    during the following iterations.  A fresh workgroup per tile instead
 //    waits for its Q and first K/V tiles and runs its epilogue alone, ~9 us
 //    of fixed cost per tile (measured on full attention at 8K and 16K).
 #include <hip/hip_runtime.h>
@@ -664,8 +665,8 @@ fwd_wide_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- epilogue
   // O / l and the LSE of a finished tile.  With several tiles per workgroup
-  // it runs after the next tile's first S (which leaves O alone), so its
-  // vector work sits beside those MFMAs; what it needs of the finished tile
+  // it runs after the next tile's first iteration (which leaves O alone),
+  // once that tile's loads are in flight; what it needs of the finished tile
   // is kept in the e_ values.
   float e_inv[QB], e_lse[QB];
   int e_qw = 0;
