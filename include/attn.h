@@ -344,9 +344,10 @@ int attn_tile_of(int p, int B, int Hq, int Hkv, int Sq, int block_m, int causal,
 
 /* Number of workgroups a dense launch uses, and query rows per tile, for
  * the layout of one query head per tile.  (Dense d = 128 inputs whose group
- * Hq / Hkv is a multiple of 4 run tiles of 64 rows of four heads instead:
- * B * (Hq / 4) * ceil(Sq / 64) workgroups, which this call, having no Hkv,
- * does not report.) */
+ * Hq / Hkv is a multiple of 4 run tiles of 64 rows of four heads instead,
+ * B * (Hq / 4) * ceil(Sq / 64) of them, on at most one workgroup per
+ * compute unit: with more tiles than compute units each workgroup runs
+ * several in turn.  This call, having no Hkv, does not report that layout.) */
 int attn_grid_size(int B, int Hq, int Sq, int d, int dtype, int* grid_out, int* block_m_out);
 
 /* Human-readable text for a status code. */
