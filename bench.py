@@ -466,8 +466,17 @@ def cpu_baseline(w, inp, budget_s, fp8_rows=None):
                 break
         sample = f"{heads} of {total} (batch, head) slices, all {w.Sq} rows each, fp64 numpy"
     dt = time.perf_counter() - t0
+    # what one whole step would take the oracle at this rate, and the FLOP it
+    # then executes: it forms every (query, key) score, masked ones included
+    step_flops = W.forward_flops(w, W.varlen_lengths(total=w.Sq) if w.varlen else None)
+    if w.varlen:
+        dense = 4.0 * w.d * w.Hq * sum(n * n for n in W.varlen_lengths(total=w.Sq))
+    else:
+        dense = 4.0 * w.d * w.B * w.Hq * w.Sq * w.Sk
     out = {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-           "sample": sample, "seconds": round(dt, 3), "blas": blas_vendor()}
+           "sample": sample, "seconds": round(dt, 3), "blas": blas_vendor(),
+           "step_seconds_at_this_rate": round(step_flops / (done_flops / dt), 1),
+           "oracle_dense_flop_per_step": dense}
     if fp8_rows is not None:
         out["fp8_c5"] = fp8_errors(fp8_rows)
     return out
@@ -617,6 +626,7 @@ def main():
             out.setdefault("other_workloads", {})[name] = ent
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds, fp8_rows)
+        out["cpu_baseline"]["gpu_speedup"] = round(tflops / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 
