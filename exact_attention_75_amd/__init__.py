@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["fwd", "fwd_ext", "bwd", "fwd_fp8", "fp8_prepass", "fp8_prepass_qkv", "fwd_splitkv", "fwd_splitkv_noalloc", "combine", "split_plan", "library",
-           "default_signs", "tile_of",
+           "default_signs", "tile_of", "load_library", "use_library",
            "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3", "ATTN_FP8_E4M3_HADAMARD", "AttnError"]
 
 ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3, ATTN_FP8_E4M3_HADAMARD = 0, 1, 2, 3
@@ -30,6 +30,9 @@ _DTYPE_NAMES = {"bf16": ATTN_BF16, "fp16": ATTN_FP16, "fp8": ATTN_FP8_E4M3,
                 "fp8_hadamard": ATTN_FP8_E4M3_HADAMARD}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# debug build whose copies poison each LDS stage before refilling it
+# (``python -m exact_attention_75_amd.build --poison``)
+POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_poison.so")
 _lib = None
 
 
@@ -42,11 +45,26 @@ class AttnError(RuntimeError):
 def library() -> ctypes.CDLL:
     """Load libattn.so (built by ``python -m exact_attention_75_amd.build``)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing; build it with python -m exact_attention_75_amd.build")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def use_library(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Route the calls of this module through the library `L` (one returned
+    by load_library, e.g. the LDS-poisoning debug build); returns the one
+    used until now."""
+    global _lib
+    prev = library()
+    _lib = L
+    return prev
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI at `path` and declare its signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with python -m exact_attention_75_amd.build")
+    L = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     L.attn_fwd.restype = I
@@ -83,7 +101,6 @@ def library() -> ctypes.CDLL:
     L.attn_clock_probe.restype = I
     L.attn_test_fail_next.argtypes = [I]
     L.attn_test_fail_next.restype = I
-    _lib = L
     return L
 
 

@@ -1,9 +1,13 @@
 """Build the HIP library libattn.so in-tree for gfx950.
 
-    python -m exact_attention_75_amd.build [--jobs N] [--save-temps DIR]
+    python -m exact_attention_75_amd.build [--jobs N] [--save-temps DIR] [--poison]
 
 Each source is compiled by hipcc to an object in ``_build/`` and the objects
-are linked into ``exact_attention_75_amd/libattn.so``.
+are linked into ``exact_attention_75_amd/libattn.so``.  ``--poison`` builds
+the LDS-poisoning debug library instead (``-DATTN_DEBUG_POISON``: every copy
+into an LDS stage first fills it with NaN), objects in ``_build_poison/``,
+library ``exact_attention_75_amd/libattn_poison.so``; the tests compare its
+results bit for bit with the normal library's.
 """
 from __future__ import annotations
 
@@ -20,6 +24,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+BUILD_POISON = os.path.join(PKG, "_build_poison")
+LIB_POISON = os.path.join(PKG, "libattn_poison.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_wide.hip", "attn_fp8.hip", "attn_combine.hip", "attn_bwd.hip",
            "attn_bwd_dkdv.hip", "attn_bwd_dq.hip", "attn_clock.hip"]
 ARCH = "gfx950"
@@ -32,8 +38,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def common_flags():
-    return [
+def common_flags(poison: bool = False):
+    return (["-DATTN_DEBUG_POISON"] if poison else []) + [
         "-O3", "-std=c++2c", "-fPIC", f"--offload-arch={ARCH}",
         # packed fp32 VALU ops stay off: the compiler must not form v_pk_* f32 ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -42,9 +48,9 @@ def common_flags():
     ]
 
 
-def compile_one(src: str, save_temps: str | None) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def compile_one(src: str, save_temps: str | None, poison: bool = False) -> str:
+    obj = os.path.join(BUILD_POISON if poison else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + common_flags(poison) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if save_temps:
@@ -68,15 +74,15 @@ def compile_one(src: str, save_temps: str | None) -> str:
 PINNED_AGPR_SOURCES = ["attn_fwd_wide.hip", "attn_bwd_dkdv.hip", "attn_bwd_dq.hip"]
 
 
-def check_pinned_agprs(src: str) -> None:
+def check_pinned_agprs(src: str, poison: bool = False) -> None:
     """Compile `src` to device assembly and fail unless, in every kernel, AGPRs
     appear only inside inline-assembly regions, nothing spills, and the kernel
     descriptor allocates every AGPR the inline assembly names (the AGPRs of a
     wave are the registers from .amdhsa_accum_offset up to
     .amdhsa_next_free_vgpr; one named past that would belong to another
     wave)."""
-    asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
-    cmd = [hipcc()] + common_flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+    asm = os.path.join(BUILD_POISON if poison else BUILD, os.path.splitext(src)[0] + ".s")
+    cmd = [hipcc()] + common_flags(poison) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"assembly listing failed: {src}\n{r.stderr}")
@@ -129,19 +135,45 @@ def scan_pinned_agprs(src: str, lines) -> None:
             raise RuntimeError(f"{src}: {m.group(1)} = {m.group(2)} (register spills)")
 
 
-def build(jobs: int = 4, save_temps: str | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def check_poison_order(src: str) -> None:
+    """In the device assembly of the poisoning build, every direct-to-LDS
+    copy must come after a poison write (ds_write_b128) that an
+    s_waitcnt lgkmcnt(0) has completed, one write per copy."""
+    asm = os.path.join(BUILD_POISON, os.path.splitext(src)[0] + ".s")
+    pending = ready = copies = 0
+    with open(asm) as f:
+        for line in f:
+            t = line.split(";")[0].strip()
+            if t.startswith("ds_write_b128"):
+                pending += 1
+            elif re.match(r"s_waitcnt\s+lgkmcnt\(0\)$", t):
+                ready, pending = ready + pending, 0
+            elif re.match(r"buffer_load_dword\w*\s.*\slds$", t):
+                copies += 1
+                if ready <= 0:
+                    raise RuntimeError(f"{src}: LDS copy without a completed poison write before it: {t}")
+                ready -= 1
+    if copies == 0:
+        raise RuntimeError(f"{src}: no direct-to-LDS copies found in the poisoning build")
+
+
+def build(jobs: int = 4, save_temps: str | None = None, poison: bool = False) -> str:
+    lib = LIB_POISON if poison else LIB
+    os.makedirs(BUILD_POISON if poison else BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: compile_one(s, save_temps), SOURCES))
-        list(ex.map(check_pinned_agprs, PINNED_AGPR_SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: compile_one(s, save_temps, poison), SOURCES))
+        list(ex.map(lambda s: check_pinned_agprs(s, poison), PINNED_AGPR_SOURCES))
+    if poison:
+        for src in PINNED_AGPR_SOURCES:
+            check_poison_order(src)
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    check_kernels(LIB)
-    return LIB
+    os.replace(tmp, lib)
+    check_kernels(lib)
+    return lib
 
 
 EXPECTED_KERNELS = ("fwd_kernel", "fwd_wide_kernel", "fwd_fp8_kernel", "prepass_kernel", "combine_kernel",
@@ -163,5 +195,6 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
     ap.add_argument("--save-temps", default=None)
+    ap.add_argument("--poison", action="store_true", help="build the LDS-poisoning debug library")
     a = ap.parse_args()
-    print(build(a.jobs, a.save_temps))
+    print(build(a.jobs, a.save_temps, a.poison))

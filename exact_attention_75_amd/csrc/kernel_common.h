@@ -11,6 +11,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -31,6 +32,24 @@ __device__ __forceinline__ float wave_half_swap(float x) {
   return __int_as_float(lane < 32 ? r[1] : r[0]);
 }
 
+// Debug build (-DATTN_DEBUG_POISON): every copy into an LDS stage first
+// fills the bytes it is about to write with 0xFF (NaN in bf16, fp16 and e4m3)
+// and waits for that write.  A copy is issued only once its stage has been
+// released (the barrier that ends the stage's last reads), so a read of a
+// stage after its release sees NaN at once, where the normal build would
+// still return the old tile's values until the copy lands.  Without such a
+// read the results are bit-identical to the normal build's; only the timing
+// moves.
+template <int N>
+__device__ __forceinline__ void poison_stage(char* dst) {
+#if defined(ATTN_DEBUG_POISON) && defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < N; ++i) *(LDS_AS i32x4*)(dst + i * 1024 + 16 * lane) = i32x4{-1, -1, -1, -1};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+}
+
 // N direct-to-LDS copies of 16 bytes per lane (buffer_load_dwordx4 ... lds):
 // copy i writes LDS bytes [dst + 1024 i, dst + 1024 (i + 1)), lane L the 16
 // bytes at offset 16 L, fetched from base + off[i].  Reads at or past `bytes`
@@ -48,6 +67,7 @@ __device__ __forceinline__ void copy_rows_to_lds(const void* base, uint32_t byte
   void* const ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+  poison_stage<N>(dst);
 #pragma unroll
   for (int i = 0; i < N; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + i * 1024), 16, off[i], 0, 0, 0);
@@ -65,6 +85,7 @@ __device__ __forceinline__ void copy_row_to_lds(const void* base, uint32_t bytes
   void* const ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+  poison_stage<1>(dst);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, off, 0, 0, 0);
 #endif
 }
@@ -116,7 +137,6 @@ __device__ __forceinline__ i16x4 lds_rd64(uint32_t addr) {
   return r;
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte LDS read issued as inline assembly (ds_read_b128), for the same
 // reason as lds_tr16; wait for it with lds_wait().

@@ -34,6 +34,18 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_poisoning_debug_build_exports_and_validates():
+    """The LDS-poisoning debug library (build --poison) exports the same
+    entry points and validates like the normal one."""
+    if not os.path.exists(ea.POISON_LIB_PATH):
+        pytest.skip("libattn_poison.so not built")
+    L = ea.load_library(ea.POISON_LIB_PATH)
+    for n in header_functions():
+        assert hasattr(L, n), n
+    assert fwd(L, d=96) == -3
+    assert fwd(L, q=None) == -1
+
+
 def fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=256, Sk=256, d=64,
              scale=0.125, causal=0, cu=None, dtype=0)
