@@ -594,12 +594,18 @@ fwd_kernel(FwdParams p) {
   // barrier, start K_{r+2} and V_{r+1} into the buffers tile r-2 used.
   auto kbuf = [&](int t) { return smem + (t % KST) * TILE; };
   auto vbuf = [&](int t) { return smem + (KST + t % STAGES) * TILE; };
+  // Two K buffers and two V stages: round 0's copies (K_1, V_0) go out
+  // together with K_0, before the first wait, so the block starts after one
+  // memory round trip instead of two.
+  constexpr bool PRE2 = STAGES == 2 && !KSINGLE;
   auto top = [&](int r) {
     if constexpr (STAGES == 2) {
       // (KSINGLE: K_{r+1} goes out at this round's second barrier instead)
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (!KSINGLE && r + 1 < ntile) issue(Kp, r + 1, kbuf(r + 1), false);
-      if (r < ntile) issue(Vp, r, vbuf(r), true);
+      if (!PRE2 || r > 0) {
+        if (!KSINGLE && r + 1 < ntile) issue(Kp, r + 1, kbuf(r + 1), false);
+        if (r < ntile) issue(Vp, r, vbuf(r), true);
+      }
     } else {
       const int prev = r >= 1 ? (int)(r + 1 < ntile) + (int)(r < ntile) : 0;  // copies of round r-1
       if (prev == 2)
@@ -617,6 +623,10 @@ fwd_kernel(FwdParams p) {
   if constexpr (STAGES == 3) {
     if (1 < ntile) issue(Kp, 1, kbuf(1), false);
     issue(Vp, 0, vbuf(0), true);
+  }
+  if constexpr (PRE2) {
+    if (1 < ntile) issue(Kp, 1, kbuf(1), false);
+    if (0 < ntile) issue(Vp, 0, vbuf(0), true);
   }
   top(0);
   f32x16 sA[NB], sB[NB];
