@@ -140,19 +140,24 @@ def check_poison_order(src: str) -> None:
     copy must come after a poison write (ds_write_b128) that an
     s_waitcnt lgkmcnt(0) has completed, one write per copy."""
     asm = os.path.join(BUILD_POISON, os.path.splitext(src)[0] + ".s")
-    pending = ready = copies = 0
     with open(asm) as f:
-        for line in f:
-            t = line.split(";")[0].strip()
-            if t.startswith("ds_write_b128"):
-                pending += 1
-            elif re.match(r"s_waitcnt\s+lgkmcnt\(0\)$", t):
-                ready, pending = ready + pending, 0
-            elif re.match(r"buffer_load_dword\w*\s.*\slds$", t):
-                copies += 1
-                if ready <= 0:
-                    raise RuntimeError(f"{src}: LDS copy without a completed poison write before it: {t}")
-                ready -= 1
+        scan_poison_order(src, f)
+
+
+def scan_poison_order(src: str, lines) -> None:
+    """The check of check_poison_order over the lines of an assembly listing."""
+    pending = ready = copies = 0
+    for line in lines:
+        t = line.split(";")[0].strip()
+        if t.startswith("ds_write_b128"):
+            pending += 1
+        elif re.match(r"s_waitcnt\s+lgkmcnt\(0\)$", t):
+            ready, pending = ready + pending, 0
+        elif re.match(r"buffer_load_dword\w*\s.*\slds$", t):
+            copies += 1
+            if ready <= 0:
+                raise RuntimeError(f"{src}: LDS copy without a completed poison write before it: {t}")
+            ready -= 1
     if copies == 0:
         raise RuntimeError(f"{src}: no direct-to-LDS copies found in the poisoning build")
 
