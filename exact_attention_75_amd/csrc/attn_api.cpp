@@ -586,7 +586,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if ((long long)Hkv * nkb > kMax32 || (long long)Hq * nqb > kMax32) return ATTN_ERR_SIZE;
   const int sq_pad = varlen ? Sq : (Sq + 31) / 32 * 32;
   void* ws = nullptr;
-  rc = workspace(kWsBwd, sizeof(float) * 2 * (size_t)(varlen ? 1 : B) * Hq * sq_pad, (hipStream_t)stream, &ws);
+  // (+32 spare pairs: the varlen dK/dV kernel reads its 32 rows of a step
+  // from one address, past the last token on the last head)
+  rc = workspace(kWsBwd, sizeof(float) * 2 * ((size_t)(varlen ? 1 : B) * Hq * sq_pad + 32), (hipStream_t)stream, &ws);
   if (rc) return rc;
   attn::BwdParams p{};
   p.q = q;

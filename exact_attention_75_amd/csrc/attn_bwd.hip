@@ -52,7 +52,9 @@ namespace attn {
 // D/8 consecutive threads own one row (16 bytes of o and dO each, one
 // coalesced row per thread group) and sum their partial dot products with
 // shuffles.  Rows i in [Sq, Sq_pad) of the statistics get (+inf, 0): P = 0
-// there.
+// there; so do the 32 spare pairs past the array (the varlen dK/dV kernel
+// reads a step's 32 rows from one address, past the last token on the last
+// head).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   typedef typename Mma<T>::vec8 vec8;
@@ -60,7 +62,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.B * p.Sq_pad * p.Hq;
   const long long rp = ((long long)blockIdx.x * 256 + threadIdx.x) / TPR;   // (b * Sq_pad + i) * Hq + h
   const int t = threadIdx.x % TPR;
-  if (rp >= rows) return;                    // whole thread groups leave together
+  if (rp >= rows) {                          // whole thread groups leave together
+    if (t == 0 && rp < rows + 32) p.stats[rp] = make_float2(__builtin_inff(), 0.f);
+    return;
+  }
   const int hq = (int)(rp % p.Hq);
   const long long bi = rp / p.Hq;
   const int i = (int)(bi % p.Sq_pad);
@@ -96,7 +101,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     pp.B = 1;
     pp.Sq_pad = p.Sq;
   }
-  const long long threads = (long long)pp.B * pp.Sq_pad * pp.Hq * (D / 8);
+  const long long threads = ((long long)pp.B * pp.Sq_pad * pp.Hq + 32) * (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

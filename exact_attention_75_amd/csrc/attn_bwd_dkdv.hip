@@ -170,9 +170,16 @@ bwd_dkdv_kernel(BwdParams p) {
     hq = hkv * p.group + hg;
     q0 = (m_begin + s % per_head) * BMQ;
   };
+  // varlen: a step's 32 (lse2, delta) pairs, one per lane of wave 0's first
+  // half, loaded with the step's copies (8-byte loads from [Hq, T]; the array
+  // has 32 spare pairs past its end, so a step's rows past the last token of
+  // the last head still read allocated, initialised memory) and written into
+  // the stage's statistics slot at the top of the step
+  float2 st_pre = make_float2(0.f, 0.f);
   auto issue = [&](int s) {
     int hq, q0;
     step_coords(s, hq, q0);
+    if (VARLEN && wave == 0 && lane < 32) st_pre = p.stats[(long long)hq * p.Sq + q_tok0 + q0 + lane];
     char* st = smem + (s & 1) * STAGE;
     const long long off = (q_tok0 + q0) * qs + hq * D;
     const uint32_t bytes = (uint32_t)(q_len - q0) * (uint32_t)qs * 2u;
@@ -195,7 +202,19 @@ bwd_dkdv_kernel(BwdParams p) {
   const float c = p.scale_log2;
   if (nsteps > 0) issue(0);
   for (int s = 0; s < nsteps; ++s) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (VARLEN) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (wave == 0 && lane < 32) {
+        // rows past the sequence take (+inf, 0): P = 0 there
+        int hq_s, q0_s;
+        step_coords(s, hq_s, q0_s);
+        const float2 v = q0_s + lane < q_len ? st_pre : make_float2(__builtin_inff(), 0.f);
+        *(float2*)(smem + (s & 1) * STAGE + 4 * QT + 8 * lane) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     if (s + 1 < nsteps) issue(s + 1);
     int hq, q0;
     step_coords(s, hq, q0);
@@ -214,23 +233,14 @@ bwd_dkdv_kernel(BwdParams p) {
     pad2(sacc, pacc);
     // register r = 4 g + i holds query 16 (g >> 1) + 8 h + 4 (g & 1) + i:
     // 4 consecutive queries per g, read as 2 x 16 bytes of (lse2, delta)
-    // (varlen: from global memory, rows past the sequence clamped to its last
-    // row -- their Q and dO are zero, so they contribute nothing)
+    // (rows past the sequence: (+inf, 0), and their Q and dO are zero)
     const float* sp = (const float*)(st + 4 * QT);
-    const float2* sg = p.stats + (long long)hq * p.Sq + q_tok0;   // varlen layout [Hq, T]
     vec8 pv[2], dsv[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qr = 16 * (g >> 1) + 8 * h + 4 * (g & 1);
       float l2[4], dl[4];
-      if constexpr (VARLEN) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float2 v2 = sg[min(q0 + qr + i, q_len - 1)];
-          l2[i] = v2.x;
-          dl[i] = v2.y;
-        }
-      } else {
+      {
         const float4 s01 = *(const float4*)(sp + 2 * qr);
         const float4 s23 = *(const float4*)(sp + 2 * qr + 4);
         l2[0] = s01.x; l2[1] = s01.z; l2[2] = s23.x; l2[3] = s23.z;
