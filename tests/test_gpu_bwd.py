@@ -236,3 +236,42 @@ def test_bwd_varlen_c4_sampled_heads(ea):
         compare("dq", sl(dq), rq, f"c4 head {h}")
         compare("dk", sl(dk), rk, f"c4 head {h}")
         compare("dv", sl(dv), rv, f"c4 head {h}")
+
+
+@pytest.mark.parametrize("dtype,d", [("fp16", 64), ("bf16", 128)])
+def test_bwd_varlen_very_negative_lse(ea, dtype, d):
+    # The first token of each sequence after the first has q = -4 k, so its
+    # (causal) row sees only itself with a score near -4 sqrt(d): its LSE is
+    # far below zero.  The dK/dV kernel's last step of the sequence before it
+    # holds rows past that sequence's end, whose statistics slots hold the
+    # next rows' pairs; those rows must get P = 0 (an exp2 of minus such an
+    # LSE overflows the 16-bit P), and every gradient must match the oracle.
+    lens = [100, 37, 300, 45]
+    Hq, Hkv = 4, 2
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = W.make_dense(1, T, T, Hq, Hkv, d, dtype, seed=91)
+    q, k, v = q[0].float(), k[0].float(), v[0].float()
+    for t0 in cu[1:-1]:
+        for h in range(Hq):
+            q[t0, h] = -4.0 * k[t0, h // (Hq // Hkv)]
+    dt = W.TORCH_DTYPES[dtype]
+    q, k, v = q.to(dt), k.to(dt), v.to(dt)
+    g = torch.Generator().manual_seed(92)
+    do = torch.randn(T, Hq, d, generator=g).to(dt)
+    scale = 1 / math.sqrt(d)
+    o_ref, l_ref = A.attention(q, k, v, scale, True, cu_seqlens=cu)
+    lows = [float(l_ref[h, t0]) for t0 in cu[1:-1] for h in range(Hq)]
+    print(f"[case] bwd varlen negative LSE {dtype} d={d}: first-token LSE {min(lows):.1f} .. {max(lows):.1f}",
+          flush=True)
+    assert max(lows) < -12.0
+    o = torch.from_numpy(o_ref).to(dt)
+    lse = torch.from_numpy(l_ref).float()
+    dev = [t.cuda() for t in (q, k, v, o, lse, do)]
+    dq, dk, dv = ea.bwd(*dev, causal=True, cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    rq, rk, rv = A.attention_backward(q, k, v, do, scale, True, cu_seqlens=cu)
+    tag = f"bwd varlen negative LSE {dtype} d{d}"
+    compare("dq", dq, rq, tag)
+    compare("dk", dk, rk, tag)
+    compare("dv", dv, rv, tag)
